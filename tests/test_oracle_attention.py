@@ -1,0 +1,180 @@
+"""Pins for oracle/attention.py (CPU only).
+
+Library routine: torch's scaled_dot_product_attention (fp64, CPU) for
+all-protected and exactly-quantizable sequences.  Closed forms: zero query,
+one dominant token, two tokens.  Brute force: every partition of a sequence
+merged by the log-sum-exp rule equals the dense softmax.  Identity: absorbed
+scoring equals unabsorbed scoring with random up-projections.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import softmax
+
+from oracle import attention, quant, layout
+from bit_mla_kv_quant_amd import synth
+
+
+def _sdpa(q, k, v, scale):
+    q = torch.from_numpy(np.asarray(q, np.float64))[None]
+    k = torch.from_numpy(np.asarray(k, np.float64))[None]
+    v = torch.from_numpy(np.asarray(v, np.float64))[None]
+    return torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=scale)[0].numpy()
+
+
+def _seq(L, seed=0, fmt="C4R4", H=16):
+    d = synth.small(fmt=fmt, batch=1, heads=H, lens=(L,), seed=seed)
+    return d.c[0], d.kr[0], d.q_lat[0], d.q_rope[0], d.scale
+
+
+# --------------------------------------------------------- protected set ---
+def test_protected_set_enumeration():
+    for L in range(0, 401):
+        m = attention.protected_mask(L)
+        idx = np.nonzero(m)[0]
+        assert len(idx) == min(L, 132)                 # union counted once
+        assert np.all(idx < L)
+        assert np.all(m[:min(4, L)])                   # sinks
+        assert np.all(m[max(0, L - 128):L])            # recent window
+        rows = layout.prot_row(idx)
+        assert len(set(rows.tolist())) == len(idx)    # distinct protection rows
+        assert np.all((rows >= 0) & (rows < 132))
+
+
+def test_effective_rows_mixing():
+    c, kr, *_ = _seq(300, seed=5)
+    rows = attention.effective_rows(c, kr, "C4R4")
+    orig = quant.bf16_to_f32(np.concatenate([c, kr], 1)).astype(np.float64)
+    deq = quant.bf16_to_f32(quant.dequantize_tokens(quant.quantize_tokens(c, kr, "C4R4")))
+    for i in (0, 3, 172, 299):
+        np.testing.assert_array_equal(rows[i], orig[i])
+    for i in (4, 100, 171):
+        np.testing.assert_array_equal(rows[i], deq[i])
+        assert np.any(rows[i] != orig[i])
+
+
+# ------------------------------------------------------ library reductions ---
+@pytest.mark.parametrize("L", [1, 2, 5, 64, 131, 132])
+def test_all_protected_equals_sdpa(L):
+    c, kr, ql, qr, scale = _seq(L, seed=L)
+    out, _ = attention.decode_sequence(c, kr, ql, qr, "C4R4", scale)
+    q = quant.bf16_to_f32(np.concatenate([ql, qr], 1))
+    k = quant.bf16_to_f32(np.concatenate([c, kr], 1))
+    ref = _sdpa(q, k, k[:, :512], scale)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_exactly_quantizable_long_sequence_equals_sdpa():
+    """Rows built on each group's code grid survive quantization unchanged, so
+    for any L the mixed-precision result equals plain attention."""
+    rng = np.random.default_rng(7)
+    L, H = 700, 16
+    codes = rng.integers(0, 16, size=(L, 9, 64))
+    codes[:, :, 0], codes[:, :, 1] = 0, 15                     # pin each group's range
+    s = 2.0 ** rng.integers(-4, 1, size=(L, 9, 1))
+    z = rng.integers(-8, 0, size=(L, 9, 1)) * 0.25
+    x = (codes * s + z).astype(np.float32).reshape(L, 576)
+    xb = quant.f32_to_bf16(x)
+    assert np.array_equal(quant.bf16_to_f32(xb), x)
+    c, kr = xb[:, :512], xb[:, 512:]
+    rows = attention.effective_rows(c, kr, "C4R4")
+    np.testing.assert_array_equal(rows, x.astype(np.float64))
+    ql = quant.f32_to_bf16(rng.normal(0, 0.07, (H, 512)).astype(np.float32))
+    qr = quant.f32_to_bf16(rng.normal(0, 0.07, (H, 64)).astype(np.float32))
+    out, _ = attention.decode_sequence(c, kr, ql, qr, "C4R4", 0.1)
+    q = quant.bf16_to_f32(np.concatenate([ql, qr], 1))
+    ref = _sdpa(q, x, x[:, :512], 0.1)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+# ------------------------------------------------------------ closed forms ---
+def test_zero_query_gives_mean_and_log_length():
+    c, kr, ql, qr, scale = _seq(1000, seed=8)
+    zl, zr = np.zeros_like(ql), np.zeros_like(qr)
+    out, lse = attention.decode_sequence(c, kr, zl, zr, "C4R4", scale)
+    rows = attention.effective_rows(c, kr, "C4R4")
+    np.testing.assert_allclose(out, np.broadcast_to(rows[:, :512].mean(0), out.shape), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, math.log(1000), rtol=1e-14)
+
+
+def test_dominant_token():
+    c, kr, ql, qr, scale = _seq(400, seed=9, H=4)
+    rows = attention.effective_rows(c, kr, "C4R4")
+    i = 250
+    ql64 = np.repeat(rows[i:i + 1, :512], 4, 0) * 50.0
+    qr64 = np.repeat(rows[i:i + 1, 512:], 4, 0) * 50.0
+    out, _ = attention.attend(ql64, qr64, rows, 1.0)
+    np.testing.assert_allclose(out, np.repeat(rows[i:i + 1, :512], 4, 0), rtol=0, atol=1e-9)
+
+
+def test_two_tokens_closed_form():
+    rows = np.zeros((2, 576))
+    rows[0, 0], rows[1, 0] = 1.0, -2.0
+    rows[0, 512], rows[1, 512] = 0.5, 0.25
+    ql = np.zeros((1, 512)); ql[0, 0] = 3.0
+    qr = np.zeros((1, 64)); qr[0, 0] = 4.0
+    s0, s1 = 0.5 * (3.0 * 1 + 4 * 0.5), 0.5 * (3.0 * -2 + 4 * 0.25)
+    out, lse = attention.attend(ql, qr, rows, 0.5)
+    p0 = 1 / (1 + math.exp(s1 - s0))
+    assert math.isclose(out[0, 0], p0 * 1 + (1 - p0) * -2, rel_tol=1e-14)
+    assert math.isclose(lse[0], math.log(math.exp(s0) + math.exp(s1)), rel_tol=1e-14)
+
+
+def test_empty_sequence():
+    out, lse = attention.attend(np.ones((2, 512)), np.ones((2, 64)), np.zeros((0, 576)), 1.0)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+# -------------------------------------------------------------- merge rule ---
+def test_partition_merge_equals_dense_softmax():
+    rng = np.random.default_rng(11)
+    c, kr, ql, qr, scale = _seq(333, seed=11)
+    rows = attention.effective_rows(c, kr, "C4R4")
+    qlf, qrf = quant.bf16_to_f32(ql) * 8.0, quant.bf16_to_f32(qr) * 8.0   # sharper softmax
+    dense_out, dense_lse = attention.attend(qlf, qrf, rows, scale)
+    for trial in range(30):
+        cuts = np.sort(rng.choice(np.arange(0, 334), size=rng.integers(1, 9), replace=True))
+        bounds = [0, *cuts.tolist(), 333]
+        parts = [attention.partial(qlf, qrf, rows[a:b], scale) for a, b in zip(bounds[:-1], bounds[1:])]
+        perm = rng.permutation(len(parts))
+        out, lse = attention.merge([parts[k] for k in perm])
+        np.testing.assert_allclose(out, dense_out, rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(lse, dense_lse, rtol=1e-13)
+
+
+def test_merge_all_empty():
+    e = attention.partial(np.ones((3, 512)), np.ones((3, 64)), np.zeros((0, 576)), 1.0)
+    out, lse = attention.merge([e, e])
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+# --------------------------------------------------------- absorption ---
+def test_absorbed_score_and_aggregation_identity():
+    """[MLA blog §4]: q^T (W_UK c) = (W_UK^T q)^T c, and W_UV sum a c = sum a W_UV c."""
+    rng = np.random.default_rng(12)
+    H, dh, L = 4, 32, 50
+    W_UK = rng.standard_normal((H, dh, 512)) / 20
+    W_UV = rng.standard_normal((H, dh, 512)) / 20
+    qC = rng.standard_normal((H, dh))
+    qR = rng.standard_normal((H, 64))
+    rows = rng.standard_normal((L, 576))
+    scale = 1 / math.sqrt(dh + 64)
+    # unabsorbed: explicit per-head content keys k^C = W_UK c and values v = W_UV c
+    kC = np.einsum("hdk,lk->hld", W_UK, rows[:, :512])
+    s_unabs = scale * (np.einsum("hd,hld->hl", qC, kC) + qR @ rows[:, 512:].T)
+    q_lat = np.einsum("hdk,hd->hk", W_UK, qC)                 # absorbed query
+    s_abs = attention.scores(q_lat, qR, rows, scale)
+    np.testing.assert_allclose(s_abs, s_unabs, rtol=1e-12, atol=1e-12)
+    p = softmax(s_unabs, axis=1)
+    v = np.einsum("hdk,lk->hld", W_UV, rows[:, :512])
+    o_unabs = np.einsum("hl,hld->hd", p, v)
+    out, _ = attention.attend(q_lat, qR, rows, scale)
+    o_abs = np.einsum("hdk,hk->hd", W_UV, out)
+    np.testing.assert_allclose(o_abs, o_unabs, rtol=1e-11, atol=1e-12)
+
+
+def test_cache_schema_576():
+    assert quant.D_ROW == 576 and quant.D_C == 512 and quant.D_R == 64

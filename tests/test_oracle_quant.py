@@ -1,0 +1,204 @@
+"""Pins for oracle/quant.py and oracle/layout.py (CPU only).
+
+Each check ties the oracle to something other than itself: torch's bf16
+conversion, exact rational arithmetic, brute-force search over all codes,
+hand-built byte patterns, and round trips.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import quant, layout
+
+
+def _torch_bf16(x):
+    t = torch.from_numpy(np.asarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _exact_round_to_bits(fr, mant_bits):
+    """Round a nonzero Fraction to the nearest binary float with `mant_bits`
+    significant bits (ties to even); normal range only.  Returns a Fraction."""
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (e - (mant_bits - 1))
+    k = a / ulp
+    lo = k.numerator // k.denominator
+    rem = k - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return sign * lo * ulp
+
+
+# ------------------------------------------------------------------ bf16 ---
+def test_bf16_rne_matches_torch_random():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * np.float32(3.0),
+        (rng.standard_normal(20000) * 1e-38).astype(np.float32),        # subnormals
+        (rng.standard_normal(20000) * 1e30).astype(np.float32),
+    ])
+    np.testing.assert_array_equal(quant.f32_to_bf16(x), _torch_bf16(x))
+
+
+def test_bf16_rne_ties_and_specials():
+    # exact ties: low 16 bits == 0x8000, both parities of the kept lsb
+    hi = np.arange(0x3F00, 0x4100, dtype=np.uint32)
+    ties = ((hi << 16) | 0x8000).view(np.float32)
+    got = quant.f32_to_bf16(ties)
+    np.testing.assert_array_equal(got, _torch_bf16(ties))
+    # ties go to the even kept pattern
+    assert np.all(got % 2 == 0)
+    specials = np.array([0.0, -0.0, np.inf, -np.inf, 3.3895313892515355e38,
+                         np.finfo(np.float32).max, 1e-45, -1e-45], dtype=np.float32)
+    np.testing.assert_array_equal(quant.f32_to_bf16(specials), _torch_bf16(specials))
+
+
+def test_bf16_rne_exact_rational():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(2000) * 10).astype(np.float32)
+    got = quant.bf16_to_f32(quant.f32_to_bf16(x))
+    for xi, gi in zip(x, got):
+        assert Fraction(float(gi)) == _exact_round_to_bits(Fraction(float(xi)), 8)
+
+
+# ------------------------------------------------------------- quantizer ---
+def _groups_small_int(rng, n, bits_range=40, spread=2.0 ** -3):
+    """Groups of bf16-exact values (small integers times a power of two): many
+    exact ties and exactly representable differences."""
+    v = rng.integers(-bits_range, bits_range + 1, size=(n, 64)).astype(np.float32) * np.float32(spread)
+    return quant.f32_to_bf16(v)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quantizer_brute_force_nearest_code(bits):
+    """Each code is the nearest of the 2^b reconstruction points q*s+z
+    (exact rational distance), ties to the even code; s and z follow the
+    stated rule."""
+    rng = np.random.default_rng(10 + bits)
+    xb = np.concatenate([_groups_small_int(rng, 300),
+                         quant.f32_to_bf16(rng.standard_normal((300, 64)).astype(np.float32))])
+    q, sb, zb = quant.quantize_groups(xb, bits)
+    m = (1 << bits) - 1
+    xf = quant.bf16_to_f32(xb)
+    for g in range(xb.shape[0]):
+        lo, hi = Fraction(float(xf[g].min())), Fraction(float(xf[g].max()))
+        # stated scale: bf16(fl32(fl32(hi-lo)/m)) -- fl32 steps via exact rounding
+        rngf = _exact_round_to_bits(hi - lo, 24)
+        s = _exact_round_to_bits(_exact_round_to_bits(rngf / m, 24), 8) if rngf != 0 else Fraction(0)
+        assert Fraction(float(quant.bf16_to_f32(sb[g]))) == s
+        assert Fraction(float(quant.bf16_to_f32(zb[g]))) == lo
+        for j in range(64):
+            x = Fraction(float(xf[g, j]))
+            if s == 0:
+                assert q[g, j] == 0
+                continue
+            d = [abs(x - (k * s + lo)) for k in range(m + 1)]
+            best = min(d)
+            cands = [k for k in range(m + 1) if d[k] == best]
+            want = cands[0] if len(cands) == 1 else [k for k in cands if k % 2 == 0][0]
+            assert q[g, j] == want, (g, j, float(x), float(s), float(lo), cands)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quantizer_invariants_on_workload_distribution(bits):
+    rng = np.random.default_rng(20 + bits)
+    a = np.exp(0.5 * rng.standard_normal(64))
+    a[:2] *= 16.0
+    xb = quant.f32_to_bf16((rng.standard_normal((5000, 64)) * a).astype(np.float32))
+    q, sb, zb = quant.quantize_groups(xb, bits)
+    m = (1 << bits) - 1
+    assert q.max() <= m and q.dtype == np.uint8
+    x = quant.bf16_to_f32(xb).astype(np.float64)
+    s = quant.bf16_to_f32(sb).astype(np.float64)
+    z = quant.bf16_to_f32(zb).astype(np.float64)
+    recon = q * s[:, None] + z[:, None]          # exact in float64
+    err = np.abs(x - recon)
+    assert np.all(err <= 0.5 * s[:, None] * (1 + 1e-6))
+    # the group minimum reconstructs exactly (code 0)
+    amin = x.argmin(axis=1)
+    assert np.all(q[np.arange(len(q)), amin] == 0)
+    xh = quant.bf16_to_f32(quant.dequantize_groups(q, sb, zb))
+    assert np.all(xh[np.arange(len(q)), amin] == x[np.arange(len(q)), amin])
+
+
+def test_constant_group_reconstructs_exactly():
+    xb = quant.f32_to_bf16(np.full((3, 64), [[1.5], [-7.0], [0.0]], dtype=np.float32))
+    for bits in (2, 4):
+        q, sb, zb = quant.quantize_groups(xb, bits)
+        assert np.all(q == 0) and np.all(sb == 0)
+        np.testing.assert_array_equal(quant.dequantize_groups(q, sb, zb), xb)
+
+
+def test_dequant_is_one_fp32_rounding_then_bf16():
+    rng = np.random.default_rng(3)
+    xb = quant.f32_to_bf16((rng.standard_normal((200, 64)) * 5).astype(np.float32))
+    q, sb, zb = quant.quantize_groups(xb, 4)
+    got = quant.bf16_to_f32(quant.dequantize_groups(q, sb, zb))
+    for g in range(0, 200, 7):
+        s = Fraction(float(quant.bf16_to_f32(sb[g])))
+        z = Fraction(float(quant.bf16_to_f32(zb[g])))
+        for j in range(64):
+            exact = int(q[g, j]) * s + z
+            want = _exact_round_to_bits(_exact_round_to_bits(exact, 24), 8)
+            assert Fraction(float(got[g, j])) == want
+
+
+# --------------------------------------------------------------- packing ---
+def test_pack_known_answer_c4():
+    codes = np.tile(np.arange(16, dtype=np.uint8), 32)[None, :]      # [1, 512]
+    p = layout.pack_content(codes, "C4R4")                              # [1, 4, 64]
+    want = np.tile(np.array([0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE], np.uint8), 8)
+    for b in range(4):
+        np.testing.assert_array_equal(p[0, b], want)
+    r = layout.pack_rope(np.arange(64, dtype=np.uint8)[None, :] % 16)
+    np.testing.assert_array_equal(r[0], want[:32])
+
+
+def test_pack_known_answer_c2():
+    codes = np.tile(np.array([0, 1, 2, 3], np.uint8), 128)[None, :]
+    p = layout.pack_content(codes, "C2R4")
+    assert p.shape == (1, 2, 64)
+    assert np.all(p == 0b11100100)
+    codes = np.zeros((1, 512), np.uint8)
+    codes[0, 256 + 4 * 5 + 2] = 3          # blk 1, byte 5, bits 4-5
+    p = layout.pack_content(codes, "C2R4")
+    assert p[0, 1, 5] == 0x30 and p.sum() == 0x30
+
+
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4"])
+def test_pack_roundtrip_and_page_roundtrip(fmt):
+    rng = np.random.default_rng(4)
+    T = 64
+    c = quant.f32_to_bf16(rng.standard_normal((T, 512)).astype(np.float32))
+    kr = quant.f32_to_bf16(rng.standard_normal((T, 64)).astype(np.float32))
+    qt = quant.quantize_tokens(c, kr, fmt)
+    np.testing.assert_array_equal(layout.unpack_content(layout.pack_content(qt["codes_c"], fmt), fmt),
+                                  qt["codes_c"])
+    np.testing.assert_array_equal(layout.unpack_rope(layout.pack_rope(qt["codes_r"])), qt["codes_r"])
+    pb = layout.page_bytes(fmt)
+    pages = np.zeros((3, pb), np.uint8)
+    slots = 2 * 64 + rng.permutation(64)
+    layout.write_tokens(pages, slots, qt, fmt)
+    assert not pages[:2].any()
+    back = layout.read_page(pages[2], fmt)
+    inv = np.argsort(slots - 128)
+    for k in ("codes_c", "codes_r", "scale", "zero"):
+        np.testing.assert_array_equal(back[k][slots - 128], qt[k])
+    del inv
+
+
+def test_page_sizes():
+    assert layout.page_bytes("C4R4") == 20736
+    assert layout.page_bytes("C2R4") == 12544
+    assert layout.PROT_ROWS * 576 * 2 == 152064
