@@ -1,0 +1,153 @@
+// C-ABI host layer of libmla_lowbit.so: argument validation (pure host code,
+// runs before any HIP call), the split plan, and dispatch to the kernels.
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/mla_lowbit.h"
+#include "internal.h"
+
+namespace mlb {
+
+static constexpr int kNumCUs = 256;       // MI355X compute units
+static constexpr int kWavesTarget = 2;    // resident decode workgroups per CU
+static constexpr int kMinPagesPerSplit = 2;
+
+static size_t page_bytes_of(int f) {
+  return f == MLA_LB_C4R4 ? 20736u : (f == MLA_LB_C2R4 ? 12544u : 0u);
+}
+
+// Split plan.  A max-length sequence of P pages is cut into nsplit splits of
+// pps pages.  Automatic choice: enough (split, sequence, head-group)
+// workgroups to keep every CU busy, but no split shorter than
+// kMinPagesPerSplit pages (each split costs a 16x512 fp32 partial write).
+Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits) {
+  Plan p{1, 1, 0};
+  const int64_t P = (static_cast<int64_t>(max_seq_len) + 63) / 64;
+  if (P <= 1) return p;
+  int64_t ns;
+  if (num_splits > 0) {
+    ns = num_splits;
+  } else {
+    const int64_t groups = static_cast<int64_t>(B) * (H / 16);
+    ns = (static_cast<int64_t>(kNumCUs) * kWavesTarget + groups - 1) / groups;
+    const int64_t cap = P / kMinPagesPerSplit;
+    if (ns > cap) ns = cap;
+  }
+  if (ns < 1) ns = 1;
+  if (ns > P) ns = P;
+  const int64_t pps = (P + ns - 1) / ns;
+  ns = (P + pps - 1) / pps;
+  p.pps = static_cast<int32_t>(pps);
+  p.nsplit = static_cast<int32_t>(ns);
+  if (ns > 1)
+    p.ws_bytes = static_cast<size_t>(B) * static_cast<size_t>(ns) * static_cast<size_t>(H) *
+                 (512 + 4) * sizeof(float);
+  return p;
+}
+
+}  // namespace mlb
+
+extern "C" {
+
+int mla_lb_version(void) { return 1; }
+
+const char* mla_lb_strerror(int code) {
+  switch (code) {
+    case MLA_LB_OK: return "ok";
+    case MLA_LB_EINVAL: return "invalid argument (null pointer or bad scalar)";
+    case MLA_LB_ESHAPE: return "unsupported or inconsistent sizes";
+    case MLA_LB_EFORMAT: return "unknown cache format";
+    case MLA_LB_EWORKSPACE: return "workspace missing or too small";
+    case MLA_LB_EHIP: return "HIP runtime error at launch";
+    default: return "unknown error code";
+  }
+}
+
+size_t mla_lb_page_bytes(int f) { return mlb::page_bytes_of(f); }
+
+size_t mla_lb_prot_bytes_per_seq(void) { return 132u * 576u * 2u; }
+
+int kv_quant_append(int f, const uint16_t* latent, const uint16_t* k_rope,
+                    const int64_t* slot_mapping, const int32_t* seq_slot, const int32_t* pos,
+                    const int32_t* new_len, int32_t T, uint8_t* pages, int64_t num_pages,
+                    uint16_t* prot, int32_t num_seq_slots, void* stream) {
+  if (f != MLA_LB_C4R4 && f != MLA_LB_C2R4) return MLA_LB_EFORMAT;
+  if (T < 0) return MLA_LB_ESHAPE;
+  if (T == 0) return MLA_LB_OK;
+  if (!latent || !k_rope || !slot_mapping || !seq_slot || !pos || !new_len || !pages || !prot)
+    return MLA_LB_EINVAL;
+  if (num_pages < 1 || num_seq_slots < 1) return MLA_LB_ESHAPE;
+  if (num_pages > (INT64_MAX / 64)) return MLA_LB_ESHAPE;
+  mlb::AppendArgs a{latent, k_rope, slot_mapping, seq_slot, pos, new_len, T,
+                    pages,  num_pages, prot, num_seq_slots};
+  return mlb::launch_append(f, a, static_cast<hipStream_t>(stream));
+}
+
+int mla_decode_lowbit_workspace(int f, int32_t B, int32_t H, int32_t max_seq_len,
+                                int32_t num_splits, size_t* bytes) {
+  if (f != MLA_LB_C4R4 && f != MLA_LB_C2R4) return MLA_LB_EFORMAT;
+  if (!bytes) return MLA_LB_EINVAL;
+  if (B < 1 || H < 16 || H > MLA_LB_MAX_HEADS || H % 16 != 0 || max_seq_len < 0 ||
+      num_splits < 0)
+    return MLA_LB_ESHAPE;
+  *bytes = mlb::make_plan(B, H, max_seq_len, num_splits).ws_bytes;
+  return MLA_LB_OK;
+}
+
+int mla_decode_lowbit(int f, const uint16_t* q_lat, const uint16_t* q_rope,
+                      const uint8_t* pages, int64_t num_pages, const uint16_t* prot,
+                      int32_t num_seq_slots, const int32_t* seq_slot,
+                      const int32_t* block_table, int32_t max_blocks,
+                      const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t H,
+                      float softmax_scale, int32_t num_splits, void* workspace,
+                      size_t workspace_bytes, float* out, float* lse, void* stream) {
+  if (f != MLA_LB_C4R4 && f != MLA_LB_C2R4) return MLA_LB_EFORMAT;
+  if (!q_lat || !q_rope || !pages || !prot || !seq_slot || !block_table || !seq_lens || !out ||
+      !lse)
+    return MLA_LB_EINVAL;
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return MLA_LB_EINVAL;
+  if (B < 1 || H < 16 || H > MLA_LB_MAX_HEADS || H % 16 != 0) return MLA_LB_ESHAPE;
+  if (max_seq_len < 0 || max_blocks < 1 || num_pages < 1 || num_seq_slots < 1 || num_splits < 0)
+    return MLA_LB_ESHAPE;
+  if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks) * 64)
+    return MLA_LB_ESHAPE;
+  if (B > 65535) return MLA_LB_ESHAPE;               // grid.y limit
+  const mlb::Plan plan = mlb::make_plan(B, H, max_seq_len, num_splits);
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return MLA_LB_EWORKSPACE;
+  float* ws = static_cast<float*>(workspace);
+  const size_t n_o = static_cast<size_t>(B) * plan.nsplit * H * 512;
+  mlb::DecodeArgs a{};
+  a.q_lat = q_lat;
+  a.q_rope = q_rope;
+  a.pages = pages;
+  a.num_pages = num_pages;
+  a.prot = prot;
+  a.num_seq_slots = num_seq_slots;
+  a.seq_slot = seq_slot;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.max_seq_len = max_seq_len;
+  a.B = B;
+  a.H = H;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.pps = plan.pps;
+  a.nsplit = plan.nsplit;
+  a.ws_o = plan.nsplit > 1 ? ws : nullptr;
+  a.ws_ml = plan.nsplit > 1 ? ws + n_o : nullptr;
+  a.out = out;
+  a.lse = lse;
+  return mlb::launch_decode(f, a, static_cast<hipStream_t>(stream));
+}
+
+int mla_lb_dequant_dump(int f, const uint8_t* pages, int64_t num_pages, int64_t page_id,
+                        uint16_t* out, void* stream) {
+  if (f != MLA_LB_C4R4 && f != MLA_LB_C2R4) return MLA_LB_EFORMAT;
+  if (!pages || !out) return MLA_LB_EINVAL;
+  if (num_pages < 1 || page_id < 0 || page_id >= num_pages) return MLA_LB_ESHAPE;
+  return mlb::launch_dequant_dump(f, pages, page_id, out, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+// kv_quant_append: the fused cache writer [QuantMLA App. C.5].
+//
+// One 64-lane wave per token; lane j owns element j of each of the nine
+// 64-wide groups (8 content groups + the RoPE group).  Per group the wave
+// reduces min/max, every lane derives the same bf16 scale and zero, computes
+// its code with IEEE fp32 subtract/divide and round-to-nearest-even
+// [QuantMLA §4.1, App. C.4], and the codes are OR-reduced across 8 (INT4) or
+// 16 (INT2) lanes into 32-bit words that one lane stores.  The token's bf16
+// row goes to its protection-buffer row when the token is protected at the
+// sequence length reached by this call.
+//
+// This translation unit is compiled with -ffp-contract=off: the quantizer's
+// subtract and divide must round exactly as specified.
+#include "common.h"
+#include "internal.h"
+
+namespace mlb {
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t or_reduce(uint32_t v, int width) {
+  for (int o = 1; o < width; o <<= 1) v |= __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Quantize one group held one element per lane.  Returns the lane's code and
+// the group's (scale, zero) bf16 bits.
+__device__ __forceinline__ uint32_t quantize_lane(float x, int bits, uint32_t& s_bits,
+                                                  uint32_t& z_bits) {
+  const float m = (float)((1 << bits) - 1);
+  const float lo = wave_min(x);
+  const float hi = wave_max(x);
+  const float rng = hi - lo;                      // fl32(hi - lo)
+  s_bits = f32_to_bf16_bits(rng / m);             // bf16(fl32(rng / m))
+  z_bits = __float_as_uint(lo) >> 16;             // lo is bf16-exact
+  const float s = bf16_bits_to_f32(s_bits);
+  if (!(s > 0.0f)) return 0u;                     // constant group: all codes 0
+  const float t = (x - lo) / s;                   // fl32(fl32(x - z) / s)
+  float q = rintf(t);                             // ties to even
+  q = fminf(fmaxf(q, 0.0f), m);
+  return (uint32_t)q;
+}
+
+template <int F>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  using FM = Fmt<F>;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int64_t slot = a.slot_mapping[t];
+  const int sq = a.seq_slot[t];
+  const int pos = a.pos[t];
+  const int new_len = a.new_len[t];
+  if (slot < 0 || slot >= a.num_pages * PAGE || sq < 0 || sq >= a.num_seq_slots || pos < 0)
+    return;                                        // wave-uniform skip
+  const int64_t page = slot / PAGE;
+  const int off = (int)(slot % PAGE);
+  uint8_t* pg = a.pages + page * FM::PAGE_BYTES;
+  const uint16_t* src_c = a.latent + (int64_t)t * DC;
+  const uint16_t* src_r = a.k_rope + (int64_t)t * DR;
+
+  uint16_t xc[NGC];
+#pragma unroll
+  for (int g = 0; g < NGC; ++g) xc[g] = src_c[64 * g + lane];
+  const uint16_t xr = src_r[lane];
+
+  // ---- content groups
+#pragma unroll
+  for (int g = 0; g < NGC; ++g) {
+    uint32_t sb, zb;
+    const uint32_t q = quantize_lane(bf16_bits_to_f32(xc[g]), FM::CBITS, sb, zb);
+    const int d = 64 * g + lane;                   // content dim
+    const int blk = d / FM::DPB;
+    const int dib = d % FM::DPB;                   // dim within block
+    if (FM::CBITS == 4) {
+      // byte k = dims 2k (lo), 2k+1 (hi): dword = dims 8w..8w+7, nibble d%8
+      const uint32_t w = or_reduce(q << (4 * (lane & 7)), 8);
+      if ((lane & 7) == 0)
+        *(uint32_t*)(pg + (blk * PAGE + off) * 64 + (dib / 8) * 4) = w;
+    } else {
+      // byte k = dims 4k+j at bits 2j: dword = dims 16w..16w+15, crumb d%16
+      const uint32_t w = or_reduce(q << (2 * (lane & 15)), 16);
+      if ((lane & 15) == 0)
+        *(uint32_t*)(pg + (blk * PAGE + off) * 64 + (dib / 16) * 4) = w;
+    }
+    if (lane == 0) *(uint32_t*)(pg + FM::OFF_MC + off * 32 + g * 4) = sb | (zb << 16);
+  }
+  // ---- RoPE group (always 4 bits)
+  {
+    uint32_t sb, zb;
+    const uint32_t q = quantize_lane(bf16_bits_to_f32(xr), 4, sb, zb);
+    const uint32_t w = or_reduce(q << (4 * (lane & 7)), 8);
+    if ((lane & 7) == 0) *(uint32_t*)(pg + FM::OFF_R + off * 32 + (lane / 8) * 4) = w;
+    if (lane == 0) *(uint32_t*)(pg + FM::OFF_MR + off * 4) = sb | (zb << 16);
+  }
+  // ---- BF16 protection row, if protected at the length reached by this call
+  if (pos < new_len && (pos < NSINK || pos >= new_len - NRECENT)) {
+    uint16_t* dst = a.prot + ((int64_t)sq * PROT_ROWS + prot_row(pos)) * DROW;
+#pragma unroll
+    for (int g = 0; g < NGC; ++g) dst[64 * g + lane] = xc[g];
+    dst[DC + lane] = xr;
+  }
+}
+
+int launch_append(int f, const AppendArgs& a, hipStream_t stream) {
+  const dim3 grid((a.T + 3) / 4), block(256);
+  if (f == 0)
+    hipLaunchKernelGGL(append_kernel<0>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(append_kernel<1>, grid, block, 0, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+}  // namespace mlb

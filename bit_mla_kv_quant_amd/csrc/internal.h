@@ -1,0 +1,60 @@
+// Internal interfaces between the C-ABI host layer (abi.cpp) and the kernel
+// translation units.  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mlb {
+
+struct AppendArgs {
+  const uint16_t* latent;
+  const uint16_t* k_rope;
+  const int64_t* slot_mapping;
+  const int32_t* seq_slot;
+  const int32_t* pos;
+  const int32_t* new_len;
+  int32_t T;
+  uint8_t* pages;
+  int64_t num_pages;
+  uint16_t* prot;
+  int32_t num_seq_slots;
+};
+
+struct DecodeArgs {
+  const uint16_t* q_lat;
+  const uint16_t* q_rope;
+  const uint8_t* pages;
+  int64_t num_pages;
+  const uint16_t* prot;
+  int32_t num_seq_slots;
+  const int32_t* seq_slot;
+  const int32_t* block_table;
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  int32_t max_seq_len;   // host bound, already min(max_seq_len, max_blocks*64)
+  int32_t B, H;
+  float scale_log2;      // softmax_scale * log2(e)
+  int32_t pps;           // pages per split
+  int32_t nsplit;        // splits of a max_seq_len sequence (grid.x)
+  float* ws_o;           // [B][nsplit][H][512] unnormalised partial outputs
+  float* ws_ml;          // [B][nsplit][H][4]   (max in log2 units, bf16-weight sum, fp32 sum, 0)
+  float* out;            // [B][H][512]
+  float* lse;            // [B][H]
+};
+
+// Split plan: how a max_seq_len sequence is cut into splits.
+struct Plan {
+  int32_t pps;       // pages per split (>= 1)
+  int32_t nsplit;    // number of splits of a max-length sequence (>= 1)
+  size_t ws_bytes;   // workspace needed (0 when nsplit == 1)
+};
+
+Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits);
+
+int launch_append(int f, const AppendArgs& a, hipStream_t stream);
+int launch_decode(int f, const DecodeArgs& a, hipStream_t stream);
+int launch_dequant_dump(int f, const uint8_t* pages, int64_t page_id, uint16_t* out,
+                        hipStream_t stream);
+
+}  // namespace mlb

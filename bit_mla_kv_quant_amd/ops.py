@@ -1,0 +1,174 @@
+"""ctypes binding of libmla_lowbit.so (argument marshalling only).
+
+Every entry point of ``include/mla_lowbit.h`` has a function of the same name
+here.  Tensors are torch tensors on the GPU; bf16 data may be passed as
+``torch.bfloat16`` or as ``torch.int16`` bit patterns.  All compute runs in the
+HIP kernels of the library; if the library is not built, importing this module
+raises -- there is no fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla_lowbit.so")
+
+FORMATS = {"C4R4": 0, "C2R4": 1}
+
+ERRORS = {0: "MLA_LB_OK", -1: "MLA_LB_EINVAL", -2: "MLA_LB_ESHAPE", -3: "MLA_LB_EFORMAT",
+          -4: "MLA_LB_EWORKSPACE", -5: "MLA_LB_EHIP"}
+
+
+class MlaLowbitError(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        msg = _lib.mla_lb_strerror(code).decode()
+        super().__init__(f"{fn} failed: {ERRORS.get(code, code)} ({msg})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m bit_mla_kv_quant_amd.build` "
+            "(hipcc, gfx950).  There is no CPU fallback.")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                          ctypes.c_float)
+    sig = {
+        "mla_lb_version": (ctypes.c_int, []),
+        "mla_lb_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        "mla_lb_page_bytes": (SZ, [ctypes.c_int]),
+        "mla_lb_prot_bytes_per_seq": (SZ, []),
+        "kv_quant_append": (ctypes.c_int, [ctypes.c_int, P, P, P, P, P, P, I32, P, I64, P, I32, P]),
+        "mla_decode_lowbit_workspace": (ctypes.c_int, [ctypes.c_int, I32, I32, I32, I32,
+                                                       ctypes.POINTER(SZ)]),
+        "mla_decode_lowbit": (ctypes.c_int, [ctypes.c_int, P, P, P, I64, P, I32, P, P, I32, P,
+                                             I32, I32, I32, F, I32, P, SZ, P, P, P]),
+        "mla_lb_dequant_dump": (ctypes.c_int, [ctypes.c_int, P, I64, I64, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+# Names the header declares (checked by the ABI tests).
+EXPORTED = ("mla_lb_version", "mla_lb_strerror", "mla_lb_page_bytes",
+            "mla_lb_prot_bytes_per_seq", "kv_quant_append", "mla_decode_lowbit_workspace",
+            "mla_decode_lowbit", "mla_lb_dequant_dump")
+
+
+def raw():
+    """The ctypes handle (for tests that drive the C ABI directly)."""
+    return _lib
+
+
+def _fmt(f):
+    return FORMATS[f] if isinstance(f, str) else int(f)
+
+
+def _ptr(t, dtypes, name):
+    if t is None:
+        return None
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+_BF16 = (torch.bfloat16, torch.int16)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(fn, code):
+    if code != 0:
+        raise MlaLowbitError(fn, code)
+
+
+def mla_lb_version():
+    return _lib.mla_lb_version()
+
+
+def mla_lb_page_bytes(fmt):
+    return _lib.mla_lb_page_bytes(_fmt(fmt))
+
+
+def mla_lb_prot_bytes_per_seq():
+    return _lib.mla_lb_prot_bytes_per_seq()
+
+
+def mla_lb_strerror(code):
+    return _lib.mla_lb_strerror(code).decode()
+
+
+def kv_quant_append(fmt, latent, k_rope, slot_mapping, seq_slot, pos, new_len, pages, prot,
+                    stream=None):
+    """Quantize and insert T tokens.  latent [T,512], k_rope [T,64] bf16;
+    slot_mapping int64 [T]; seq_slot, pos, new_len int32 [T];
+    pages uint8 [num_pages, page_bytes]; prot bf16 [num_seq_slots, 132, 576]."""
+    T = latent.shape[0]
+    code = _lib.kv_quant_append(
+        _fmt(fmt), _ptr(latent, _BF16, "latent"), _ptr(k_rope, _BF16, "k_rope"),
+        _ptr(slot_mapping, (torch.int64,), "slot_mapping"),
+        _ptr(seq_slot, (torch.int32,), "seq_slot"), _ptr(pos, (torch.int32,), "pos"),
+        _ptr(new_len, (torch.int32,), "new_len"), T,
+        _ptr(pages, (torch.uint8,), "pages"), pages.shape[0],
+        _ptr(prot, _BF16, "prot"), prot.shape[0], _stream(stream))
+    _check("kv_quant_append", code)
+
+
+def mla_decode_lowbit_workspace(fmt, B, H, max_seq_len, num_splits=0):
+    n = ctypes.c_size_t(0)
+    _check("mla_decode_lowbit_workspace",
+           _lib.mla_decode_lowbit_workspace(_fmt(fmt), B, H, max_seq_len, num_splits,
+                                            ctypes.byref(n)))
+    return n.value
+
+
+def mla_decode_lowbit(fmt, q_lat, q_rope, pages, prot, seq_slot, block_table, seq_lens,
+                      max_seq_len, softmax_scale, num_splits=0, workspace=None, out=None,
+                      lse=None, stream=None):
+    """Decode attention; returns (out fp32 [B,H,512], lse fp32 [B,H])."""
+    B, H = q_lat.shape[0], q_lat.shape[1]
+    dev = q_lat.device
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    need = mla_decode_lowbit_workspace(fmt, B, H, max_seq_len, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    code = _lib.mla_decode_lowbit(
+        _fmt(fmt), _ptr(q_lat, _BF16, "q_lat"), _ptr(q_rope, _BF16, "q_rope"),
+        _ptr(pages, (torch.uint8,), "pages"), pages.shape[0], _ptr(prot, _BF16, "prot"),
+        prot.shape[0], _ptr(seq_slot, (torch.int32,), "seq_slot"),
+        _ptr(block_table, (torch.int32,), "block_table"), block_table.shape[1],
+        _ptr(seq_lens, (torch.int32,), "seq_lens"), int(max_seq_len), B, H,
+        float(softmax_scale), int(num_splits),
+        None if workspace is None else ctypes.c_void_p(workspace.data_ptr()), ws_bytes,
+        _ptr(out, (torch.float32,), "out"), _ptr(lse, (torch.float32,), "lse"), _stream(stream))
+    _check("mla_decode_lowbit", code)
+    return out, lse
+
+
+def mla_lb_dequant_dump(fmt, pages, page_id, out=None, stream=None):
+    """bf16 bits [64, 576] (int16) reconstructed by the decode kernel for one page."""
+    if out is None:
+        out = torch.empty((64, 576), dtype=torch.int16, device=pages.device)
+    _check("mla_lb_dequant_dump",
+           _lib.mla_lb_dequant_dump(_fmt(fmt), _ptr(pages, (torch.uint8,), "pages"),
+                                    pages.shape[0], int(page_id), _ptr(out, _BF16, "out"),
+                                    _stream(stream)))
+    return out

@@ -1,0 +1,195 @@
+/*
+ * mla_lowbit.h -- C ABI of libmla_lowbit.so: native low-bit MLA decode
+ * (QuantMLA-style C4R4 / C2R4 caches) for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [QuantMLA x]  "QuantMLA: Function-Aligned Dual-Path Quantization for
+ *                 Low-Bit MLA KV Caching", section x.
+ *   [MLA blog x]  "DeepSeek MLA: low-rank KV cache and inference efficiency"
+ *                 (weigao.cc), section x.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns all
+ *     memory, including workspaces; the library allocates nothing and keeps
+ *     no state between calls.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Results are visible after the caller synchronizes.
+ *   - Return value: MLA_LB_OK (0) or a negative error code.  Shape, pointer
+ *     and size checks run on the host BEFORE any HIP call, so a rejected call
+ *     touches neither the GPU nor its arguments.  A failed launch returns
+ *     MLA_LB_EHIP.  No exception crosses the ABI.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Device-side guards: tokens whose slot / sequence slot / page id fall
+ *     outside the sizes passed in are skipped (never dereferenced).  Such
+ *     inputs give unspecified results, not memory faults.  NaN/Inf inputs and
+ *     overlapping slots are outside the defined domain.
+ *
+ * Cache format (one physical page = 64 token slots; slot = page*64 + offset)
+ *   [QuantMLA App. C.4/C.5], [MLA blog §6].  Structure-of-arrays, every
+ *   region starting at a multiple of 256 bytes:
+ *     codes_c  C4R4: [4 blk][64 tok][64 B], blk = content dims 128*blk..+127,
+ *                    byte k holds dims 2k (bits 0-3) and 2k+1 (bits 4-7)
+ *              C2R4: [2 blk][64 tok][64 B], blk = content dims 256*blk..+255,
+ *                    byte k holds dim 4k+j in bits 2j..2j+1
+ *     codes_r  [64 tok][32 B], byte k holds RoPE dims 2k (lo) and 2k+1 (hi)
+ *     meta_c   [64 tok][8 groups][scale, zero] bf16
+ *     meta_r   [64 tok][scale, zero] bf16
+ *   Page bytes: C4R4 20736 (324 per token), C2R4 12544 (196 per token).
+ *
+ * Quantizer [QuantMLA §4.1, App. C.4] (per token, per group of 64 values x,
+ * m = 2^bits - 1, all arithmetic IEEE fp32, round-to-nearest-even):
+ *     s = bf16(fl32(fl32(max x - min x) / m)),  z = min x (bf16-exact),
+ *     q = clamp(rint(fl32(fl32(x - z) / s)), 0, m), or q = 0 when s == 0,
+ *     reconstruction x^ = bf16(fl32(q * s + z)).
+ * Content groups use bits 4 (C4R4) or 2 (C2R4); the RoPE group uses 4 bits.
+ *
+ * BF16 protection buffer [QuantMLA §3.3, App. C.5]: per sequence slot,
+ * prot[132][576] bf16, a row = [c (512) | k_R (64)].  Token position i < 4
+ * uses row i; i >= 4 uses row 4 + (i mod 128).  For a sequence of length L
+ * the protected set is [0, min(4,L)) U [max(0, L-128), L): those tokens are
+ * read from prot, all others from their packed copy.
+ */
+#ifndef MLA_LOWBIT_H
+#define MLA_LOWBIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Cache formats, CxRy = x-bit content cache, y-bit RoPE-key cache
+ * [QuantMLA §4.1]. */
+typedef enum { MLA_LB_C4R4 = 0, MLA_LB_C2R4 = 1 } mla_lb_format;
+
+enum {
+  MLA_LB_OK = 0,
+  MLA_LB_EINVAL = -1,     /* null pointer or invalid scalar argument */
+  MLA_LB_ESHAPE = -2,     /* unsupported or inconsistent sizes       */
+  MLA_LB_EFORMAT = -3,    /* unknown mla_lb_format                   */
+  MLA_LB_EWORKSPACE = -4, /* workspace missing or too small          */
+  MLA_LB_EHIP = -5        /* HIP runtime error at launch             */
+};
+
+enum {
+  MLA_LB_D_C = 512,        /* content latent width  [MLA blog §1]      */
+  MLA_LB_D_R = 64,         /* RoPE key width        [MLA blog §3]      */
+  MLA_LB_PAGE_TOKENS = 64, /* tokens per page       [QuantMLA App. C.5] */
+  MLA_LB_PROT_ROWS = 132,  /* 4 sink + 128 recent   [QuantMLA App. C.5] */
+  MLA_LB_MAX_HEADS = 128
+};
+
+/* Library ABI version (host, pure). */
+int mla_lb_version(void);
+
+/* Static message for an error code (host, pure, never NULL). */
+const char* mla_lb_strerror(int code);
+
+/* Bytes of one physical page of format f (20736 / 12544), 0 if f is unknown
+ * (host, pure). */
+size_t mla_lb_page_bytes(int f);
+
+/* Bytes of one sequence slot's protection buffer: 132*576*2 = 152064
+ * (host, pure). */
+size_t mla_lb_prot_bytes_per_seq(void);
+
+/*
+ * kv_quant_append -- the fused cache writer [QuantMLA App. C.5]: quantize
+ * each new token's content latent and post-RoPE key in groups of 64, pack the
+ * codes and the bf16 (scale, zero) metadata into its slot, and refresh the
+ * BF16 protection buffer.  A packed copy is written for every token, including
+ * protected ones, so a token leaving the recent window switches to its packed
+ * copy with no requantization.
+ *
+ *   latent       [T][512] bf16   content latent c of each token
+ *   k_rope       [T][64]  bf16   decoupled RoPE key, already rotated
+ *   slot_mapping [T] int64       physical page * 64 + offset; must be in
+ *                                [0, num_pages*64); distinct within a call
+ *   seq_slot     [T] int32       protection-buffer slot of the token's sequence,
+ *                                in [0, num_seq_slots)
+ *   pos          [T] int32       zero-based position of the token in its sequence
+ *   new_len      [T] int32       length of the token's sequence once every token
+ *                                of this call is in.  The bf16 row of token
+ *                                `pos` is written iff pos is in the protected set
+ *                                of that length, so a call may carry many tokens
+ *                                of one sequence (a whole prompt) without two of
+ *                                them racing for a ring row.
+ *   T            >= 0 tokens (T == 0 is a no-op)
+ *   pages        [num_pages][page_bytes(f)] bytes (written at the token slots)
+ *   prot         [num_seq_slots][132][576] bf16 (rows written as above)
+ * Tokens with an out-of-range slot, seq_slot, or pos < 0 are skipped.
+ */
+int kv_quant_append(int f, const uint16_t* latent, const uint16_t* k_rope,
+                    const int64_t* slot_mapping, const int32_t* seq_slot,
+                    const int32_t* pos, const int32_t* new_len, int32_t T,
+                    uint8_t* pages, int64_t num_pages, uint16_t* prot,
+                    int32_t num_seq_slots, void* stream);
+
+/*
+ * mla_decode_lowbit_workspace -- bytes of workspace mla_decode_lowbit needs
+ * for the same (f, B, H, max_seq_len, num_splits) (host, pure).  Zero when
+ * the call runs in one pass (a single split per sequence).
+ *   bytes (host out)
+ */
+int mla_decode_lowbit_workspace(int f, int32_t B, int32_t H, int32_t max_seq_len,
+                                int32_t num_splits, size_t* bytes);
+
+/*
+ * mla_decode_lowbit -- decode attention over the mixed-precision cache
+ * [QuantMLA §3.3, App. C.5], absorbed MLA form [MLA blog §4]:
+ *
+ *   S[b,h,i] = softmax_scale * (q_lat[b,h] . c~_i + q_rope[b,h] . k~_R,i)
+ *   out[b,h] = sum_i softmax_i(S[b,h,:]) c~_i          (512-d latent output)
+ *   lse[b,h] = ln sum_i exp(S[b,h,i])
+ *
+ * over i in [0, seq_lens[b]), one global softmax per (b, h), where
+ * (c~_i, k~_R,i) is the protected bf16 row for i in the protected set and the
+ * reconstruction from the packed copy otherwise.  Packed codes are unpacked
+ * and dequantized inside the kernel; no bf16 history or per-head K/V is
+ * formed.  Scores and aggregation run on bf16 matrix cores with fp32
+ * accumulation.  The sequence is split across compute units and the partial
+ * (max, sum, unnormalised output) triples are merged by the log-sum-exp rule
+ * [QuantMLA App. C.5, App. F.1 (split-result combination)].
+ *
+ *   q_lat        [B][H][512] bf16   absorbed query (W_UK^T q^C)
+ *   q_rope       [B][H][64]  bf16   post-RoPE query part
+ *   pages, num_pages, prot, num_seq_slots: as in kv_quant_append
+ *   seq_slot     [B] int32          protection-buffer slot of each sequence
+ *   block_table  [B][max_blocks] int32  physical page of logical block j
+ *   seq_lens     [B] int32 (device) tokens in each sequence, including the
+ *                                   token being decoded; clamped on device to
+ *                                   [0, min(max_seq_len, max_blocks*64)]
+ *   max_seq_len  host upper bound of seq_lens (sizes the split plan)
+ *   B >= 1; H a multiple of 16, 16 <= H <= 128
+ *   softmax_scale  > 0, finite
+ *   num_splits   0 = automatic, else the number of splits a max_seq_len
+ *                sequence is cut into (>= 1)
+ *   workspace    device buffer of at least mla_decode_lowbit_workspace(...)
+ *                bytes (may be NULL when that size is 0)
+ *   out          [B][H][512] fp32
+ *   lse          [B][H] fp32, natural log; -inf for an empty sequence (whose
+ *                out row is 0)
+ */
+int mla_decode_lowbit(int f, const uint16_t* q_lat, const uint16_t* q_rope,
+                      const uint8_t* pages, int64_t num_pages, const uint16_t* prot,
+                      int32_t num_seq_slots, const int32_t* seq_slot,
+                      const int32_t* block_table, int32_t max_blocks,
+                      const int32_t* seq_lens, int32_t max_seq_len, int32_t B,
+                      int32_t H, float softmax_scale, int32_t num_splits,
+                      void* workspace, size_t workspace_bytes, float* out,
+                      float* lse, void* stream);
+
+/*
+ * mla_lb_dequant_dump -- write the bf16 rows the decode kernel reconstructs
+ * for every slot of one page, [64][576] = [c^ | k^_R], using the same device
+ * code as mla_decode_lowbit.  For checking the reconstruction bit for bit.
+ *   page_id in [0, num_pages)
+ */
+int mla_lb_dequant_dump(int f, const uint8_t* pages, int64_t num_pages,
+                        int64_t page_id, uint16_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_LOWBIT_H */

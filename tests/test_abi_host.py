@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_lowbit.h")
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from bit_mla_kv_quant_amd import ops as o
+    return o
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, re.M)))
+
+
+def test_header_declares_expected_calls(ops):
+    fns = header_functions()
+    assert set(fns) == set(ops.EXPORTED), fns
+
+
+def test_library_exports_every_declared_symbol(ops):
+    out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for fn in header_functions():
+        assert fn in syms, fn
+        assert getattr(ops.raw(), fn)
+
+
+def test_pure_host_queries(ops):
+    assert ops.mla_lb_version() >= 1
+    assert ops.mla_lb_page_bytes("C4R4") == 20736
+    assert ops.mla_lb_page_bytes("C2R4") == 12544
+    assert ops.mla_lb_page_bytes(7) == 0
+    assert ops.mla_lb_prot_bytes_per_seq() == 152064
+    for c in (0, -1, -2, -3, -4, -5, -99):
+        assert isinstance(ops.mla_lb_strerror(c), str) and ops.mla_lb_strerror(c)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+
+
+def _append(lib, f=0, T=4, null=None, num_pages=1, nslots=1):
+    args = [FAKE] * 6
+    if null is not None:
+        args[null] = None
+    return lib.kv_quant_append(f, *args, T, FAKE, num_pages, FAKE, nslots, None)
+
+
+def test_append_validation(ops):
+    lib = ops.raw()
+    assert _append(lib, f=5) == -3
+    assert _append(lib, T=-1) == -2
+    assert lib.kv_quant_append(0, None, None, None, None, None, None, 0, None, 0, None, 0, None) == 0
+    for k in range(6):
+        assert _append(lib, null=k) == -1
+    assert _append(lib, num_pages=0) == -2
+    assert _append(lib, nslots=0) == -2
+
+
+def _decode(lib, f=0, B=2, H=16, max_blocks=4, msl=200, scale=0.07, ns=0, ws=None, ws_bytes=0,
+            null=None, num_pages=8, nslots=2):
+    ptrs = {"q_lat": FAKE, "q_rope": FAKE, "pages": FAKE, "prot": FAKE, "seq_slot": FAKE,
+            "block_table": FAKE, "seq_lens": FAKE, "out": FAKE, "lse": FAKE}
+    if null:
+        ptrs[null] = None
+    return lib.mla_decode_lowbit(f, ptrs["q_lat"], ptrs["q_rope"], ptrs["pages"], num_pages,
+                                 ptrs["prot"], nslots, ptrs["seq_slot"], ptrs["block_table"],
+                                 max_blocks, ptrs["seq_lens"], msl, B, H, scale, ns, ws,
+                                 ws_bytes, ptrs["out"], ptrs["lse"], None)
+
+
+def test_decode_validation(ops):
+    lib = ops.raw()
+    assert _decode(lib, f=2) == -3
+    for k in ("q_lat", "q_rope", "pages", "prot", "seq_slot", "block_table", "seq_lens", "out", "lse"):
+        assert _decode(lib, null=k) == -1, k
+    assert _decode(lib, scale=0.0) == -1
+    assert _decode(lib, scale=float("inf")) == -1
+    assert _decode(lib, scale=float("nan")) == -1
+    for H in (0, 8, 24, 144, 256):
+        assert _decode(lib, H=H) == -2, H
+    assert _decode(lib, B=0) == -2
+    assert _decode(lib, msl=257, max_blocks=4) == -2        # seq longer than the block table
+    assert _decode(lib, msl=-1) == -2
+    assert _decode(lib, ns=-1) == -2
+    assert _decode(lib, num_pages=0) == -2
+    assert _decode(lib, nslots=0) == -2
+    # a split plan needs a workspace: none / too small -> EWORKSPACE
+    need = ops.mla_decode_lowbit_workspace("C4R4", 2, 16, 200, 2)
+    assert need == 2 * 2 * 16 * 516 * 4
+    assert _decode(lib, ns=2, ws=None) == -4
+    assert _decode(lib, ns=2, ws=FAKE, ws_bytes=need - 1) == -4
+
+
+def test_dequant_dump_validation(ops):
+    lib = ops.raw()
+    assert lib.mla_lb_dequant_dump(3, FAKE, 4, 0, FAKE, None) == -3
+    assert lib.mla_lb_dequant_dump(0, None, 4, 0, FAKE, None) == -1
+    assert lib.mla_lb_dequant_dump(0, FAKE, 4, 4, FAKE, None) == -2
+    assert lib.mla_lb_dequant_dump(0, FAKE, 4, -1, FAKE, None) == -2
+
+
+def test_workspace_plan(ops):
+    # single page or num_splits=1: one pass, no workspace
+    assert ops.mla_decode_lowbit_workspace("C4R4", 4, 16, 64, 0) == 0
+    assert ops.mla_decode_lowbit_workspace("C4R4", 4, 16, 100000, 1) == 0
+    # automatic plans always fit the max-length sequence in <= 2*256 workgroups' worth of splits
+    for (B, H, L) in [(1, 16, 1024), (32, 16, 8192), (64, 16, 32768), (16, 128, 32768), (8, 128, 131080)]:
+        n = ops.mla_decode_lowbit_workspace("C4R4", B, H, L, 0)
+        assert n % (B * H * 516 * 4) == 0
+    with pytest.raises(ops.MlaLowbitError):
+        ops.mla_decode_lowbit_workspace("C4R4", 1, 20, 100, 0)
