@@ -1,0 +1,361 @@
+"""Benchmark of the low-bit MLA decode hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config N] [--no-cpu] [--no-graph]
+
+One step = one decode step of a whole batch through the C ABI:
+kv_quant_append of each sequence's current token (quantize, pack, slot-mapped
+insert, BF16 window refresh), then mla_decode_lowbit over every cached token
+(paged low-bit + BF16 protected rows, one global softmax, split-KV merge).
+The headline workload is the DeepSeek-V2-Lite-shaped C4R4 cache: batch 32,
+16 heads, 8192 tokens per sequence, 64-token pages with a shuffled block table.
+
+Inputs are synthetic and seeded (bit_mla_kv_quant_amd.synth), uploaded before
+timing.  To keep the 256 MB last-level cache from serving the KV history, the
+bench cycles R full replicas of every input (pages, protection buffers,
+queries, tables) whose total exceeds 1 GiB; step i uses replica i mod R.
+Each replica's step is captured once in a HIP graph and replayed.
+
+Printed: ONE JSON line with the KV-tokens/s of the whole step, plus
+  roofline      the decode call's algorithmic bytes / its average duration
+                (HIP events around back-to-back decode-only replays on the
+                stream they run on), against the 8 TB/s HBM peak;
+  cpu_baseline  the CPU oracle decoding a bounded sample of the same workload
+                on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "low-bit MLA decode KV-tokens/s + achieved HBM TB/s vs MI355X peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PAGE = 64
+PROT_ROWS = 132
+ROW_BYTES = 576 * 2            # one bf16 cache row [c | k_R]
+TOKEN_BYTES = {"C4R4": 324, "C2R4": 196}   # packed codes + bf16 (scale, zero) per token
+KERNEL_SOURCES = ("bit_mla_kv_quant_amd/csrc/decode.hip", "bit_mla_kv_quant_amd/csrc/common.h")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def n_protected(L):
+    return min(L, 4) + max(0, min(128, L - 4)) if L > 0 else 0
+
+
+def algorithmic_bytes(fmt, lens, H):
+    """Bytes the decode call must move: packed history of unprotected tokens,
+    bf16 rows of protected ones, queries, outputs, block-table entries."""
+    kv = sum((L - n_protected(L)) * TOKEN_BYTES[fmt] + n_protected(L) * ROW_BYTES for L in lens)
+    B = len(lens)
+    q = B * H * 576 * 2
+    out = B * H * 513 * 4
+    bt = sum(-(-L // PAGE) * 4 for L in lens)
+    return kv + q + out + bt
+
+
+def algorithmic_flops(lens, H):
+    return sum(lens) * H * 2 * (576 + 512)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload):
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, or None if absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# --------------------------------------------------------------- workload ---
+def upload(ops, torch, d, fmt, dev):
+    """Page pool + protection buffers filled through kv_quant_append with the
+    first L_b - 1 tokens of every sequence (the L_b-th is the step's token)."""
+    B = d.B
+    pb = ops.mla_lb_page_bytes(fmt)
+    pages = torch.zeros((d.num_pages, pb), dtype=torch.uint8, device=dev)
+    prot = torch.zeros((B, PROT_ROWS, 576), dtype=torch.int16, device=dev)
+
+    def i16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
+
+    seq_slot = torch.arange(B, dtype=torch.int32, device=dev)
+    for b in range(B):
+        L = int(d.lens[b]) - 1
+        if L <= 0:
+            continue
+        P = np.arange(L, dtype=np.int64)
+        ops.kv_quant_append(
+            fmt, i16(d.c[b][:L]), i16(d.kr[b][:L]),
+            torch.from_numpy(d.slots(b, P)).to(dev),
+            torch.full((L,), b, dtype=torch.int32, device=dev),
+            torch.from_numpy(P.astype(np.int32)).to(dev),
+            torch.full((L,), L, dtype=torch.int32, device=dev), pages, prot)
+    # the step's own token per sequence: position L_b - 1, sequence length L_b
+    lastpos = (d.lens.astype(np.int64) - 1)
+    step = {
+        "latent": i16(np.stack([d.c[b][lastpos[b]] for b in range(B)])),
+        "k_rope": i16(np.stack([d.kr[b][lastpos[b]] for b in range(B)])),
+        "slot": torch.from_numpy(np.array([d.slots(b, [lastpos[b]])[0] for b in range(B)],
+                                          dtype=np.int64)).to(dev),
+        "seq_slot": seq_slot,
+        "pos": torch.from_numpy(lastpos.astype(np.int32)).to(dev),
+        "new_len": torch.from_numpy(d.lens.astype(np.int32)).to(dev),
+    }
+    torch.cuda.synchronize()
+    return {
+        "pages": pages, "prot": prot, "seq_slot": seq_slot,
+        "block_table": torch.from_numpy(d.block_table).to(dev),
+        "seq_lens": torch.from_numpy(d.lens.astype(np.int32)).to(dev),
+        "q_lat": i16(d.q_lat), "q_rope": i16(d.q_rope), "step": step,
+    }
+
+
+def clone_replica(torch, r):
+    out = {}
+    for k, v in r.items():
+        out[k] = {kk: vv.clone() for kk, vv in v.items()} if isinstance(v, dict) else v.clone()
+    return out
+
+
+def footprint(r):
+    n = 0
+    for v in r.values():
+        vals = v.values() if isinstance(v, dict) else [v]
+        n += sum(t.numel() * t.element_size() for t in vals)
+    return n
+
+
+# ------------------------------------------------------------ cpu leg ------
+def cpu_baseline(d, fmt, budget_s=12.0):
+    """The CPU oracle (as it stands) decoding whole sequences of the same
+    workload, cycling through the batch, until about budget_s seconds of work
+    are done (at least one sequence)."""
+    from oracle import attention
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: numpy's BLAS default
+        threads = len(os.sched_getaffinity(0))
+    tokens, nseq, t0 = 0, 0, time.perf_counter()
+    while True:
+        b = nseq % d.B
+        L = int(d.lens[b])
+        attention.decode_sequence(d.c[b][:L], d.kr[b][:L], d.q_lat[b], d.q_rope[b], fmt, d.scale)
+        tokens += L
+        nseq += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(tokens / dt, 1), "unit": "KV-tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{nseq} sequence decodes cycling over the {d.B} sequences of the same "
+                      f"workload ({tokens} KV tokens, {d.H} heads): fp32 quantize/dequant of "
+                      f"every token + fp64 attention, {dt:.1f} s on {threads} BLAS threads"}
+
+
+# ------------------------------------------------------------------ main ---
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, help="synthetic workload id (0-4)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graphs")
+    ap.add_argument("--min-rotation-gib", type=float, default=1.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one device copy of this size (HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the decode path has no multi-GPU leg in this library.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_mla_kv_quant_amd import ops, synth   # raises if libmla_lowbit.so is missing
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.config]
+    fmt = wl.fmt
+    log("workload", wl.name, "drawing")
+    d = synth.draw(wl, extra_tokens=0)
+    lens = [int(x) for x in d.lens]
+    B, H = d.B, d.H
+    max_len = max(lens)
+
+    log("uploading + filling cache through kv_quant_append")
+    base = upload(ops, torch, d, fmt, dev)
+    fp = footprint(base)
+    R = max(1, math.ceil(args.min_rotation_gib * (1 << 30) / fp))
+    reps = [base] + [clone_replica(torch, base) for _ in range(R - 1)]
+    torch.cuda.synchronize()
+    log(f"replicas {R} x {fp / 2**20:.1f} MiB")
+
+    ws_bytes = ops.mla_decode_lowbit_workspace(fmt, B, H, max_len, 0)
+    for r in reps:
+        r["ws"] = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        r["out"] = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
+        r["lse"] = torch.empty((B, H), dtype=torch.float32, device=dev)
+
+    stream = torch.cuda.Stream()   # default priority
+
+    def do_append(r):
+        s = r["step"]
+        ops.kv_quant_append(fmt, s["latent"], s["k_rope"], s["slot"], s["seq_slot"], s["pos"],
+                            s["new_len"], r["pages"], r["prot"], stream=stream)
+
+    def do_decode(r):
+        ops.mla_decode_lowbit(fmt, r["q_lat"], r["q_rope"], r["pages"], r["prot"], r["seq_slot"],
+                              r["block_table"], r["seq_lens"], max_len, d.scale, 0,
+                              workspace=r["ws"] if ws_bytes else None, out=r["out"],
+                              lse=r["lse"], stream=stream)
+
+    def do_step(r):
+        do_append(r)
+        do_decode(r)
+
+    use_graph = not args.no_graph
+    steps_fn, dec_fn = [], []
+    if use_graph:
+        with torch.cuda.stream(stream):
+            for r in reps:          # one eager pass first (warms the library)
+                do_step(r)
+        stream.synchronize()
+        for r in reps:
+            g1, g2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g1, stream=stream):
+                do_step(r)
+            with torch.cuda.graph(g2, stream=stream):
+                do_decode(r)
+            steps_fn.append(g1.replay)
+            dec_fn.append(g2.replay)
+        graphs_keepalive = steps_fn, dec_fn  # noqa: F841
+    else:
+        steps_fn = [(lambda r=r: do_step(r)) for r in reps]
+        dec_fn = [(lambda r=r: do_decode(r)) for r in reps]
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            dst.copy_(src)
+        stream.synchronize()
+        log(f"copy probe: {n} bytes read + {n} bytes written")
+        del src, dst
+
+    # ---- warmup
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            steps_fn[i % R]()
+    stream.synchronize()
+
+    # ---- timed region: exactly K steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            steps_fn[i % R]()
+    stream.synchronize()
+    torch.cuda.synchronize()
+    t_steps = time.perf_counter() - t0
+    ms_per_step = 1e3 * t_steps / args.steps
+    kv_tokens = sum(lens)
+    value = kv_tokens / (t_steps / args.steps)
+
+    # ---- decode-only launches, HIP events on the stream they run on
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        for i in range(min(args.warmup, R)):
+            dec_fn[i % R]()
+        ev0.record(stream)
+        for i in range(args.steps):
+            dec_fn[i % R]()
+        ev1.record(stream)
+    ev1.synchronize()
+    dec_ms = ev0.elapsed_time(ev1) / args.steps
+    ab = algorithmic_bytes(fmt, lens, H)
+    fl = algorithmic_flops(lens, H)
+    achieved_gbs = ab / (dec_ms * 1e-3) / 1e9
+    achieved_tflops = fl / (dec_ms * 1e-3) / 1e12
+    # which roof binds: bytes at 8 TB/s vs flops at 2.5 PF
+    mfma_bound = fl / (BF16_PEAK_TFLOPS * 1e12) > ab / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(achieved_tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved_tflops / BF16_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = stored_traffic(wl.name)
+    roof["kernel"] = "mla_decode_lowbit (decode_kernel + combine_kernel)"
+    roof["algorithmic_bytes_per_launch"] = ab
+    roof["algorithmic_flops_per_launch"] = fl
+    roof["launch_ms"] = round(dec_ms, 5)
+    roof["hbm_frac"] = round(achieved_gbs / HBM_PEAK_GBS, 4)
+
+    # ---- append-only timing (context)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for i in range(args.steps):
+            do_append(reps[i % R])
+        ev1.record(stream)
+    ev1.synchronize()
+    app_ms = ev0.elapsed_time(ev1) / args.steps
+
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "KV-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "format": fmt, "batch": B, "heads": H,
+                   "context": [min(lens), max(lens)], "page_tokens": PAGE,
+                   "d_c": 512, "d_r": 64, "sink": 4, "recent": 128, "replicas": R,
+                   "hip_graph": use_graph, "parallelism": "split-kv on 1 GPU",
+                   "step": "kv_quant_append(B tokens) + mla_decode_lowbit"},
+        "roofline": roof,
+        "decode_kv_tokens_per_s": round(kv_tokens / (dec_ms * 1e-3), 1),
+        "append_ms": round(app_ms, 5),
+        "packed_bytes_per_token": TOKEN_BYTES[fmt], "bf16_bytes_per_token": ROW_BYTES,
+    }
+    if not args.no_cpu:
+        log("cpu oracle leg")
+        res["cpu_baseline"] = cpu_baseline(d, fmt)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
