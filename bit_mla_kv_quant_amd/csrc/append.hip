@@ -5,7 +5,8 @@
 // reduces min/max, every lane derives the same bf16 scale and zero, computes
 // its code with IEEE fp32 subtract/divide and round-to-nearest-even
 // [QuantMLA §4.1, App. C.4], and the codes are OR-reduced across 8 (INT4) or
-// 16 (INT2) lanes into 32-bit words that one lane stores.  The token's bf16
+// 16 (INT2) lanes into 32-bit words that one lane stores (bit positions as in
+// the page layout of include/mla_lowbit.h).  The token's bf16
 // row goes to its protection-buffer row when the token is protected at the
 // sequence length reached by this call.
 //
@@ -86,8 +87,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       if ((lane & 7) == 0)
         *(uint32_t*)(pg + (blk * PAGE + off) * 64 + (dib / 8) * 4) = w;
     } else {
-      // byte k = dims 4k+j at bits 2j: dword = dims 16w..16w+15, crumb d%16
-      const uint32_t w = or_reduce(q << (2 * (lane & 15)), 16);
+      // dword = dims 16w..16w+15: dim 16w+2m at bits 2m, dim 16w+2m+1 at
+      // bits 16+2m
+      const int e = lane & 15;
+      const uint32_t w = or_reduce(q << (16 * (e & 1) + 2 * (e >> 1)), 16);
       if ((lane & 15) == 0)
         *(uint32_t*)(pg + (blk * PAGE + off) * 64 + (dib / 16) * 4) = w;
     }

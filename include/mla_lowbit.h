@@ -30,7 +30,9 @@
  *     codes_c  C4R4: [4 blk][64 tok][64 B], blk = content dims 128*blk..+127,
  *                    byte k holds dims 2k (bits 0-3) and 2k+1 (bits 4-7)
  *              C2R4: [2 blk][64 tok][64 B], blk = content dims 256*blk..+255,
- *                    byte k holds dim 4k+j in bits 2j..2j+1
+ *                    little-endian 32-bit word k holds dims 16k..16k+15:
+ *                    dim 16k+2m in bits 2m..2m+1, dim 16k+2m+1 in bits
+ *                    16+2m..17+2m (m = 0..7)
  *     codes_r  [64 tok][32 B], byte k holds RoPE dims 2k (lo) and 2k+1 (hi)
  *     meta_c   [64 tok][8 groups][scale, zero] bf16
  *     meta_r   [64 tok][scale, zero] bf16
@@ -164,7 +166,8 @@ int mla_decode_lowbit_workspace(int f, int32_t B, int32_t H, int32_t max_seq_len
  *   B >= 1; H a multiple of 16, 16 <= H <= 128
  *   softmax_scale  > 0, finite
  *   num_splits   0 = automatic, else the number of splits a max_seq_len
- *                sequence is cut into (>= 1)
+ *                sequence is cut into (>= 1); raised where needed so that no
+ *                split spans more than 256 pages (16384 tokens)
  *   workspace    device buffer of at least mla_decode_lowbit_workspace(...)
  *                bytes (may be NULL when that size is 0)
  *   out          [B][H][512] fp32

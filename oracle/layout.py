@@ -18,8 +18,12 @@ offsets multiples of 256 bytes:
   region   C4R4                         C2R4
   codes_c  [4 blk][64 tok][64 B]        [2 blk][64 tok][64 B]
            blk = content dims 128*blk..   blk = content dims 256*blk..
-           byte k: dims 2k (bits 0-3),    byte k: dim 4k+j at bits 2j..2j+1
-                   2k+1 (bits 4-7)
+           byte k: dims 2k (bits 0-3),    little-endian 32-bit word k holds
+                   2k+1 (bits 4-7)        dims 16k..16k+15: dim 16k+2m at
+                                          bits 2m..2m+1 and dim 16k+2m+1 at
+                                          bits 16+2m..17+2m (m = 0..7), so
+                                          each pair of neighbouring dims sits
+                                          16 bits apart
   codes_r  [64 tok][32 B]  byte k: RoPE dims 2k (bits 0-3), 2k+1 (bits 4-7)
   meta_c   [64 tok][8 grp][2] bf16 (scale, zero), little endian
   meta_r   [64 tok][2] bf16 (scale, zero)
@@ -70,9 +74,12 @@ def pack_content(codes_c, fmt):
         # blk b covers dims 128b..128b+127; byte k = dims 2k (lo), 2k+1 (hi)
         q = q.reshape(T, 4, 64, 2)
         return (q[..., 0] | (q[..., 1] << 4)).astype(np.uint8)
-    # C2R4: blk b covers dims 256b..256b+255; byte k = dims 4k+j at bits 2j
-    q = q.reshape(T, 2, 64, 4)
-    return (q[..., 0] | (q[..., 1] << 2) | (q[..., 2] << 4) | (q[..., 3] << 6)).astype(np.uint8)
+    # C2R4: blk b covers dims 256b..256b+255 as 16 words of 16 dims; within a
+    # word, dim 2m goes to bits 2m and dim 2m+1 to bits 16+2m
+    q = q.reshape(T, 2, 16, 8, 2).astype(np.uint32)
+    shift_even = (2 * np.arange(8, dtype=np.uint32))
+    words = ((q[..., 0] << shift_even) | (q[..., 1] << (shift_even + 16))).sum(axis=-1)
+    return words.astype("<u4").view(np.uint8).reshape(T, 2, 64)
 
 
 def unpack_content(packed, fmt):
@@ -80,10 +87,12 @@ def unpack_content(packed, fmt):
     p = np.asarray(packed, dtype=np.uint8)
     T = p.shape[0]
     if fmt == "C4R4":
-        out = np.stack([p & 0xF, p >> 4], axis=-1)
-    else:
-        out = np.stack([(p >> (2 * j)) & 0x3 for j in range(4)], axis=-1)
-    return out.reshape(T, D_C).astype(np.uint8)
+        return np.stack([p & 0xF, p >> 4], axis=-1).reshape(T, D_C).astype(np.uint8)
+    words = np.ascontiguousarray(p).view("<u4").reshape(T, 2, 16, 1).astype(np.uint32)
+    shift_even = (2 * np.arange(8, dtype=np.uint32))
+    even = (words >> shift_even) & 3
+    odd = (words >> (shift_even + 16)) & 3
+    return np.stack([even, odd], axis=-1).reshape(T, D_C).astype(np.uint8)
 
 
 def pack_rope(codes_r):

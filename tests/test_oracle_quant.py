@@ -166,14 +166,24 @@ def test_pack_known_answer_c4():
 
 
 def test_pack_known_answer_c2():
+    # dim d carries code d % 4: in every 16-dim word the even dims hold
+    # 0,2,0,2,... (bits 0..15 = 0x8888) and the odd dims 1,3,1,3,...
+    # (bits 16..31 = 0xDDDD); little-endian bytes 88 88 DD DD.
     codes = np.tile(np.array([0, 1, 2, 3], np.uint8), 128)[None, :]
     p = layout.pack_content(codes, "C2R4")
     assert p.shape == (1, 2, 64)
-    assert np.all(p == 0b11100100)
+    np.testing.assert_array_equal(p[0, 0], np.tile(np.array([0x88, 0x88, 0xDD, 0xDD], np.uint8), 16))
+    np.testing.assert_array_equal(p[0, 1], p[0, 0])
+    # one code: blk 1, dim 87 = word 5, odd dim of pair m = 3 -> bits 22-23
+    # of word 5 -> byte 4*5 + 2, value 0xC0
     codes = np.zeros((1, 512), np.uint8)
-    codes[0, 256 + 4 * 5 + 2] = 3          # blk 1, byte 5, bits 4-5
+    codes[0, 256 + 87] = 3
     p = layout.pack_content(codes, "C2R4")
-    assert p[0, 1, 5] == 0x30 and p.sum() == 0x30
+    assert p[0, 1, 22] == 0xC0 and int(p.sum()) == 0xC0
+    codes = np.zeros((1, 512), np.uint8)
+    codes[0, 16 * 3 + 2 * 7] = 2            # blk 0, word 3, even dim m = 7 -> bits 14-15
+    p = layout.pack_content(codes, "C2R4")
+    assert p[0, 0, 4 * 3 + 1] == 0x80 and int(p.sum()) == 0x80
 
 
 @pytest.mark.parametrize("fmt", ["C4R4", "C2R4"])
