@@ -21,8 +21,7 @@ static size_t page_bytes_of(int f) {
 // pps pages.  Automatic choice: enough (split, sequence, head-group)
 // workgroups to keep every CU busy, but no split shorter than
 // kMinPagesPerSplit pages (each split costs a 16x512 fp32 partial write).
-// A requested or automatic count is raised so that no split exceeds
-// MAX_PAGES_PER_SPLIT pages.
+
 Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits) {
   Plan p{1, 1, 0};
   const int64_t P = (static_cast<int64_t>(max_seq_len) + 63) / 64;
@@ -38,9 +37,6 @@ Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits) {
   }
   if (ns < 1) ns = 1;
   if (ns > P) ns = P;
-  // no split longer than the kernel's page-id buffer
-  const int64_t min_ns = (P + MAX_PAGES_PER_SPLIT - 1) / MAX_PAGES_PER_SPLIT;
-  if (ns < min_ns) ns = min_ns;
   const int64_t pps = (P + ns - 1) / ns;
   ns = (P + pps - 1) / pps;
   p.pps = static_cast<int32_t>(pps);

@@ -7,18 +7,19 @@
 // q * s is exact in fp32 (q < 16, s has an 8-bit significand), so one fused
 // multiply-add rounds exactly once, like the unfused product-then-sum.
 //
-// Lane geometry (one wave = 16 token slots x 4 lane groups): lane
-// (n16 = lane % 16, g = lane / 16) owns token slot `tt` of the page and, per
-// content chunk r, a contiguous run of SPAN dims (one 64-dim group or half of
-// one); the dims are delivered as slices of 8 consecutive bf16, the unit a
-// lane contributes to one v_mfma_f32_16x16x32_bf16 B operand.
+// Lane geometry: a lane owns one token slot `tt` of a page and, in dim half
+// dh (0 or 1), lane group g (0..3): the 64 content dims 256*dh + 64*g ..+63
+// (exactly one quantization group) and the 8 RoPE dims 32*dh + 8*g ..+7.
+// Dims are delivered as slices of 8 consecutive bf16, the unit a lane
+// contributes to one v_mfma_f32_16x16x32_bf16 operand.
 #pragma once
 #include "common.h"
 
 namespace mlb {
 
-// Keeps the compiler from folding a mask into later byte extractions, so each
-// byte of the masked word is converted by one v_cvt_f32_ubyteN.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Keeps the compiler from folding a mask into later byte extractions.
 __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   asm("" : "+v"(x));
   return x;
@@ -29,14 +30,35 @@ __device__ __forceinline__ float ubyte(uint32_t w, int k) {
 }
 
 // 8 INT4 codes of one 32-bit word (byte k: dim 2k in bits 0-3, dim 2k+1 in
-// bits 4-7) -> 8 consecutive reconstructed bf16 values.
-__device__ __forceinline__ bf16x8 deq_int4x8(uint32_t w, float s, float z) {
+// bits 4-7) -> 8 consecutive reconstructed bf16 values; one byte conversion
+// per code.  Valid for every finite scale.
+__device__ __forceinline__ bf16x8 deq_int4x8_ubyte(uint32_t w, float s, float z) {
   const uint32_t lo = opaque(w & 0x0F0F0F0Fu);          // dims 0,2,4,6
   const uint32_t hi = opaque((w >> 4) & 0x0F0F0F0Fu);   // dims 1,3,5,7
   u32x4 r;
 #pragma unroll
   for (int k = 0; k < 4; ++k)
     r[k] = pack_bf16x2(__builtin_fmaf(ubyte(lo, k), s, z), __builtin_fmaf(ubyte(hi, k), s, z));
+  return bitcast<bf16x8>(r);
+}
+
+// Same values, two codes per conversion: a byte b in 0..15 read as an OCP
+// fp8 e4m3 number is exactly b * 2^-9 (the subnormal range and the first
+// normal binade share the spacing 2^-9), so with s9 = s * 2^9 (exact)
+// fma(b * 2^-9, s9, z) equals fma(b, s, z) bit for bit.  Needs s9 finite,
+// i.e. s < 2^119; callers route larger scales to the byte path.
+__device__ __forceinline__ bf16x8 deq_int4x8_fp8(uint32_t w, float s9, float z) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;                  // dims 0,2,4,6
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;           // dims 1,3,5,7
+  const f32x2_t l01 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);   // dims 0,2
+  const f32x2_t l23 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);    // dims 4,6
+  const f32x2_t h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);   // dims 1,3
+  const f32x2_t h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);    // dims 5,7
+  u32x4 r;
+  r[0] = pack_bf16x2(__builtin_fmaf(l01[0], s9, z), __builtin_fmaf(h01[0], s9, z));
+  r[1] = pack_bf16x2(__builtin_fmaf(l01[1], s9, z), __builtin_fmaf(h01[1], s9, z));
+  r[2] = pack_bf16x2(__builtin_fmaf(l23[0], s9, z), __builtin_fmaf(h23[0], s9, z));
+  r[3] = pack_bf16x2(__builtin_fmaf(l23[1], s9, z), __builtin_fmaf(h23[1], s9, z));
   return bitcast<bf16x8>(r);
 }
 
@@ -75,30 +97,34 @@ __device__ __forceinline__ void deq_int2x16(uint32_t w, const Lut2& lut, bf16x8&
 // ---------------------------------------------------------------- pages ----
 // Register image of one lane's share of one token slot of a packed page.
 template <int F> struct Packed;
-template <> struct Packed<0> {   // C4R4: chunk r = dims 128r + 32g .. +31
-  u32x4 c[4];
-  uint32_t mc[4];                // (scale, zero) bf16 pair of chunk r's group
-  u32x2 rc;                      // RoPE dims 16g .. 16g+15
-  uint32_t mr;
+template <> struct Packed<0> {   // C4R4
+  u32x4 c[2];                    // content dims 256dh+64g .. +63 (2 x 32 dims)
+  uint32_t mc;                   // (scale, zero) bf16 pair of that group
+  uint32_t rc;                   // RoPE dims 32dh+8g .. +7
+  uint32_t mr;                   // RoPE (scale, zero)
 };
-template <> struct Packed<1> {   // C2R4: chunk r = dims 256r + 64g .. +63
-  u32x4 c[2];
-  uint32_t mc[2];
-  u32x2 rc;
+template <> struct Packed<1> {   // C2R4
+  u32x4 c;                       // content dims 256dh+64g .. +63
+  uint32_t mc;
+  uint32_t rc;
   uint32_t mr;
 };
 
 template <int F>
-__device__ __forceinline__ Packed<F> load_packed(const uint8_t* pg, int tt, int g) {
+__device__ __forceinline__ Packed<F> load_packed(const uint8_t* pg, int tt, int dh, int g) {
   using FM = Fmt<F>;
   Packed<F> p;
-#pragma unroll
-  for (int r = 0; r < FM::NBLK; ++r) {
-    p.c[r] = *(const u32x4*)(pg + (r * PAGE + tt) * 64 + g * 16);
-    const int grp = (r * FM::DPB + g * (FM::DPB / 4)) / 64;
-    p.mc[r] = *(const uint32_t*)(pg + FM::OFF_MC + tt * 32 + grp * 4);
+  if constexpr (F == 0) {
+    // blocks of 128 dims: block 2dh + g/2, bytes 32*(g&1) .. +31 of the row
+    const uint8_t* row = pg + ((2 * dh + (g >> 1)) * PAGE + tt) * 64 + 32 * (g & 1);
+    p.c[0] = *(const u32x4*)row;
+    p.c[1] = *(const u32x4*)(row + 16);
+  } else {
+    // blocks of 256 dims: block dh, bytes 16g .. +15 of the row
+    p.c = *(const u32x4*)(pg + (dh * PAGE + tt) * 64 + 16 * g);
   }
-  p.rc = *(const u32x2*)(pg + FM::OFF_R + tt * 32 + g * 8);
+  p.mc = *(const uint32_t*)(pg + FM::OFF_MC + tt * 32 + (4 * dh + g) * 4);
+  p.rc = *(const uint32_t*)(pg + FM::OFF_R + tt * 32 + 16 * dh + 4 * g);
   p.mr = *(const uint32_t*)(pg + FM::OFF_MR + tt * 4);
   return p;
 }
@@ -106,26 +132,38 @@ __device__ __forceinline__ Packed<F> load_packed(const uint8_t* pg, int tt, int 
 __device__ __forceinline__ float meta_scale(uint32_t m) { return bf16_bits_to_f32(m & 0xffffu); }
 __device__ __forceinline__ float meta_zero(uint32_t m) { return bf16_bits_to_f32(m >> 16); }
 
-// Content chunk r -> NT slices of 8 bf16 (NT = 4 for C4R4, 8 for C2R4).
+// 8 INT4 codes with the fp8 conversion when the scale allows it.
+__device__ __forceinline__ bf16x8 deq_int4x8(uint32_t w, uint32_t meta) {
+  const float s = meta_scale(meta), z = meta_zero(meta);
+  const float s9 = s * 512.0f;
+  if (__builtin_expect(s9 <= 3.4028234663852886e38f, 1)) return deq_int4x8_fp8(w, s9, z);
+  return deq_int4x8_ubyte(w, s, z);
+}
+
+// The lane's 64 content dims -> 8 slices of 8 bf16 (dims 8t .. 8t+7 of them).
 template <int F>
-__device__ __forceinline__ void deq_content(const Packed<F>& p, int r, bf16x8* kv) {
-  const float s = meta_scale(p.mc[r]), z = meta_zero(p.mc[r]);
+__device__ __forceinline__ void deq_content(const Packed<F>& p, bf16x8* kv) {
   if constexpr (F == 0) {
+    const float s = meta_scale(p.mc), z = meta_zero(p.mc);
+    const float s9 = s * 512.0f;
+    if (__builtin_expect(s9 <= 3.4028234663852886e38f, 1)) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) kv[t] = deq_int4x8(p.c[r][t], s, z);
+      for (int t = 0; t < 8; ++t) kv[t] = deq_int4x8_fp8(p.c[t >> 2][t & 3], s9, z);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) kv[t] = deq_int4x8_ubyte(p.c[t >> 2][t & 3], s, z);
+    }
   } else {
-    const Lut2 lut = make_lut2(s, z);
+    const Lut2 lut = make_lut2(meta_scale(p.mc), meta_zero(p.mc));
 #pragma unroll
-    for (int t = 0; t < 4; ++t) deq_int2x16(p.c[r][t], lut, kv[2 * t], kv[2 * t + 1]);
+    for (int k = 0; k < 4; ++k) deq_int2x16(p.c[k], lut, kv[2 * k], kv[2 * k + 1]);
   }
 }
 
-// RoPE dims 16g .. 16g+15 -> two slices of 8 bf16.
+// The lane's 8 RoPE dims -> one slice of 8 bf16.
 template <int F>
-__device__ __forceinline__ void deq_rope(const Packed<F>& p, bf16x8* kr) {
-  const float s = meta_scale(p.mr), z = meta_zero(p.mr);
-  kr[0] = deq_int4x8(p.rc[0], s, z);
-  kr[1] = deq_int4x8(p.rc[1], s, z);
+__device__ __forceinline__ bf16x8 deq_rope(const Packed<F>& p) {
+  return deq_int4x8(p.rc, p.mr);
 }
 
 }  // namespace mlb

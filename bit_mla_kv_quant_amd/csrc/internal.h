@@ -43,10 +43,6 @@ struct DecodeArgs {
   float* lse;            // [B][H]
 };
 
-// Longest split, in pages (the decode kernel keeps the split's physical page
-// ids in LDS).
-constexpr int MAX_PAGES_PER_SPLIT = 256;
-
 // Split plan: how a max_seq_len sequence is cut into splits.
 struct Plan {
   int32_t pps;       // pages per split (>= 1)

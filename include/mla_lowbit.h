@@ -166,8 +166,7 @@ int mla_decode_lowbit_workspace(int f, int32_t B, int32_t H, int32_t max_seq_len
  *   B >= 1; H a multiple of 16, 16 <= H <= 128
  *   softmax_scale  > 0, finite
  *   num_splits   0 = automatic, else the number of splits a max_seq_len
- *                sequence is cut into (>= 1); raised where needed so that no
- *                split spans more than 256 pages (16384 tokens)
+ *                sequence is cut into (>= 1)
  *   workspace    device buffer of at least mla_decode_lowbit_workspace(...)
  *                bytes (may be NULL when that size is 0)
  *   out          [B][H][512] fp32
