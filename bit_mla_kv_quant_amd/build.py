@@ -30,6 +30,7 @@ COMMON = [
 UNITS = {
     "append.hip": ["-ffp-contract=off"],
     "decode.hip": [],
+    "decode_h128.hip": [],
     "abi.cpp": ["-x", "hip"],
 }
 

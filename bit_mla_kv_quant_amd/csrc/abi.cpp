@@ -12,15 +12,17 @@ namespace mlb {
 static constexpr int kNumCUs = 256;       // MI355X compute units
 static constexpr int kWavesTarget = 1;    // resident decode workgroups per CU
 static constexpr int kMinPagesPerSplit = 2;
+static constexpr int kMinPagesPerSplit128 = 8;   // 128-head blocks write 256 KB per split
 
 static size_t page_bytes_of(int f) {
   return f == MLA_LB_C4R4 ? 20736u : (f == MLA_LB_C2R4 ? 12544u : 0u);
 }
 
 // Split plan.  A max-length sequence of P pages is cut into nsplit splits of
-// pps pages.  Automatic choice: enough (split, sequence, head-group)
-// workgroups to keep every CU busy, but no split shorter than
-// kMinPagesPerSplit pages (each split costs a 16x512 fp32 partial write).
+// pps pages.  Automatic choice: enough (split, sequence, head-block)
+// workgroups to keep every CU busy, but no split shorter than a minimum
+// number of pages (each split costs a heads x 512 fp32 partial write).  Head
+// blocks are 128 heads when H is a multiple of 128, else 16.
 
 Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits) {
   Plan p{1, 1, 0};
@@ -30,9 +32,10 @@ Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits) {
   if (num_splits > 0) {
     ns = num_splits;
   } else {
-    const int64_t groups = static_cast<int64_t>(B) * (H / 16);
+    const bool h128 = H % 128 == 0;
+    const int64_t groups = static_cast<int64_t>(B) * (h128 ? H / 128 : H / 16);
     ns = (static_cast<int64_t>(kNumCUs) * kWavesTarget + groups - 1) / groups;
-    const int64_t cap = P / kMinPagesPerSplit;
+    const int64_t cap = P / (h128 ? kMinPagesPerSplit128 : kMinPagesPerSplit);
     if (ns > cap) ns = cap;
   }
   if (ns < 1) ns = 1;

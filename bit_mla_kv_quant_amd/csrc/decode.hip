@@ -449,12 +449,17 @@ __global__ __launch_bounds__(512) void dequant_dump_kernel(const uint8_t* pages,
 }
 
 int launch_decode(int f, const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.nsplit, a.B, a.H / 16), block(512);
-  if (f == 0)
-    hipLaunchKernelGGL(decode16_kernel<0>, grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode16_kernel<1>, grid, block, 0, stream, a);
-  if (hipGetLastError() != hipSuccess) return -5;
+  if (a.H % 128 == 0) {
+    // 128-head blocks: one reconstruction of each page serves all heads
+    if (launch_decode128(f, a, stream) != 0) return -5;
+  } else {
+    const dim3 grid(a.nsplit, a.B, a.H / 16), block(512);
+    if (f == 0)
+      hipLaunchKernelGGL(decode16_kernel<0>, grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL(decode16_kernel<1>, grid, block, 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return -5;
+  }
   if (a.nsplit > 1) {
     hipLaunchKernelGGL(combine_kernel, dim3(DC / 64, a.H / 16, a.B), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return -5;

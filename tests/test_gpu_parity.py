@@ -157,6 +157,32 @@ def test_sharp_attention():
     check_decode(d, c, out, lse, d.lens)
 
 
+@pytest.mark.parametrize("H", [16, 128])
+def test_score_jumps(H):
+    """Tokens whose score for one head lies far above everything before them
+    (2^100 and 2^190 in weight, in the packed and the protected region): the
+    running reference maximum must move without losing the earlier tokens."""
+    d = synth.small(fmt="C4R4", batch=2, heads=H, lens=(1500, 900), seed=31)
+    l2e = 1.4426950408889634
+
+    def plant(b, pos, head, log2_score):
+        q = quant.bf16_to_f32(d.q_lat[b, head]).astype(np.float64)
+        alpha = log2_score / (np.linalg.norm(q) ** 2 * d.scale * l2e)
+        d.c[b][pos] = quant.f32_to_bf16((alpha * q).astype(np.float32))
+        d.kr[b][pos] = 0
+
+    plant(0, 300, 0, 100.0)      # packed, far beyond the first chunk's maximum
+    plant(0, 1200, 0, 190.0)     # packed, far beyond again
+    plant(1, 890, H - 1, 120.0)  # protected recent-window row
+    say("score_jumps", H)
+    c = GpuCache(d)
+    c.fill()
+    for ns in (1, 0, 5):
+        out, lse = c.decode(num_splits=ns)
+        w = check_decode(d, c, out, lse, d.lens)
+        say("  num_splits", ns, "worst rel-L2", f"{w:.2e}")
+
+
 @pytest.mark.parametrize("fmt", ["C4R4", "C2R4"])
 def test_token_aging(fmt):
     """Append one token per step from L=1 to 300 and decode each step: a
