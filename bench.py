@@ -44,7 +44,9 @@ PAGE = 64
 PROT_ROWS = 132
 ROW_BYTES = 576 * 2            # one bf16 cache row [c | k_R]
 TOKEN_BYTES = {"C4R4": 324, "C2R4": 196}   # packed codes + bf16 (scale, zero) per token
-KERNEL_SOURCES = ("bit_mla_kv_quant_amd/csrc/decode.hip", "bit_mla_kv_quant_amd/csrc/common.h")
+KERNEL_SOURCES = ("bit_mla_kv_quant_amd/csrc/decode.hip", "bit_mla_kv_quant_amd/csrc/decode_h16.hip",
+                  "bit_mla_kv_quant_amd/csrc/decode_h128.hip", "bit_mla_kv_quant_amd/csrc/dequant.h",
+                  "bit_mla_kv_quant_amd/csrc/common.h")
 
 
 def log(*a):
@@ -319,7 +321,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)}
     roof["traffic"] = stored_traffic(wl.name)
-    roof["kernel"] = "mla_decode_lowbit (decode_kernel + combine_kernel)"
+    roof["kernel"] = ("mla_decode_lowbit (decode128_kernel + combine_kernel)" if H % 128 == 0
+                      else "mla_decode_lowbit (decode16w_kernel + combine_kernel)")
     roof["algorithmic_bytes_per_launch"] = ab
     roof["algorithmic_flops_per_launch"] = fl
     roof["launch_ms"] = round(dec_ms, 5)

@@ -31,6 +31,7 @@ UNITS = {
     "append.hip": ["-ffp-contract=off"],
     "decode.hip": [],
     "decode_h128.hip": [],
+    "decode_h16.hip": [],
     "abi.cpp": ["-x", "hip"],
 }
 

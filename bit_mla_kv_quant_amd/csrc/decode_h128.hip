@@ -53,41 +53,6 @@ constexpr int HB = 128;              // heads per workgroup
 constexpr float REF_HEADROOM_LOG2 = 64.0f;   // weights stay below 2^64 (fp32-safe sums)
 constexpr float FP8_PATH_MAX_SCALE9 = 3.4028234663852886e38f;
 
-// One lane's share of one token slot: content groups 2g, 2g+1 and RoPE dims
-// 16g .. 16g+15 (page layout as written by kv_quant_append).
-template <int F> struct Slot;
-template <> struct Slot<0> {     // C4R4
-  u32x4 c[4];                    // dims 128g .. 128g+127 (block g of the page)
-  u32x2 r;                       // RoPE dims 16g .. 16g+15
-  u32x2 mc;                      // (scale, zero) of groups 2g, 2g+1
-  uint32_t mr;                   // RoPE (scale, zero)
-};
-template <> struct Slot<1> {     // C2R4
-  u32x4 c[2];                    // dims 128g .. 128g+127 (half of block g/2)
-  u32x2 r;
-  u32x2 mc;
-  uint32_t mr;
-};
-
-template <int F>
-__device__ __forceinline__ Slot<F> load_slot(const uint8_t* pg, int tt, int g) {
-  using FM = Fmt<F>;
-  Slot<F> p;
-  if constexpr (F == 0) {
-    const uint8_t* row = pg + (g * PAGE + tt) * 64;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p.c[i] = *(const u32x4*)(row + 16 * i);
-  } else {
-    const uint8_t* row = pg + ((g >> 1) * PAGE + tt) * 64 + 32 * (g & 1);
-    p.c[0] = *(const u32x4*)row;
-    p.c[1] = *(const u32x4*)(row + 16);
-  }
-  p.r = *(const u32x2*)(pg + FM::OFF_R + tt * 32 + 8 * g);
-  p.mc = *(const u32x2*)(pg + FM::OFF_MC + tt * 32 + 8 * g);
-  p.mr = *(const uint32_t*)(pg + FM::OFF_MR + tt * 4);
-  return p;
-}
-
 // max over the two lanes of a head (l and l ^ 32)
 __device__ __forceinline__ float pair_max(float x) {
   const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
@@ -155,7 +120,7 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
 
   // ---- reconstruct page k (physical id `phys`) from `cur` into tile k & 1:
   // row tt, content dims 128g .. 128g+127 and RoPE dims 16g .. 16g+15.
-  auto build = [&](auto ordinary_tag, const Slot<F>& cur, const int k, const int phys) {
+  auto build = [&](auto ordinary_tag, const LaneSlot<F>& cur, const int k, const int phys) {
     constexpr bool ORDINARY = decltype(ordinary_tag)::value;
     uint16_t* row = ktile[k & 1] + tt * KT_PITCH;
     uint16_t* rc = row + 128 * g;
@@ -216,7 +181,7 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
     }
   };
   // Is page k ordinary for this wave (decided from its packed metadata)?
-  auto ordinary = [&](const Slot<F>& cur, const int k, const int phys) -> bool {
+  auto ordinary = [&](const LaneSlot<F>& cur, const int k, const int phys) -> bool {
     const int p = p0 + k;
     if (phys < 0 || p * PAGE < NSINK || (p + 1) * PAGE > L - NRECENT) return false;
     bool fits = meta_scale(cur.mr) * 512.0f <= FP8_PATH_MAX_SCALE9;
@@ -225,7 +190,7 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
              meta_scale(cur.mc[1]) * 512.0f <= FP8_PATH_MAX_SCALE9;
     return !__any(!fits);
   };
-  auto build_page = [&](const Slot<F>& cur, const int k, const int phys) {
+  auto build_page = [&](const LaneSlot<F>& cur, const int k, const int phys) {
     if (ordinary(cur, k, phys)) build(std::true_type{}, cur, k, phys);
     else build(std::false_type{}, cur, k, phys);
   };
@@ -311,15 +276,15 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
     f_run = 0.f;
     if (threadIdx.x == 0) redo_flag = 0;
     int id_k = page_id(0), id_k1 = page_id(min(1, np - 1));
-    Slot<F> cur = load_slot<F>(page_ptr(id_k), tt, g);
+    LaneSlot<F> cur = load_lane_slot<F>(page_ptr(id_k), tt, g);
     build_page(cur, 0, id_k);
-    cur = load_slot<F>(page_ptr(id_k1), tt, g);
+    cur = load_lane_slot<F>(page_ptr(id_k1), tt, g);
     __syncthreads();
     for (int k = 0; k < np; ++k) {
       const int id_k2 = page_id(min(k + 2, np - 1));
       if (k + 1 < np) {
         build_page(cur, k + 1, id_k1);
-        cur = load_slot<F>(page_ptr(id_k2), tt, g);
+        cur = load_lane_slot<F>(page_ptr(id_k2), tt, g);
       }
       attend(k, id_k);
       __syncthreads();

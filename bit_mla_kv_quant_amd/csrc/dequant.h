@@ -129,6 +129,42 @@ __device__ __forceinline__ Packed<F> load_packed(const uint8_t* pg, int tt, int 
   return p;
 }
 
+// One lane's share of one token slot when four lanes share a token: lane g
+// takes content groups 2g, 2g+1 (dims 128g .. 128g+127) and RoPE dims
+// 16g .. 16g+15 (page layout as written by kv_quant_append).
+template <int F> struct LaneSlot;
+template <> struct LaneSlot<0> {     // C4R4
+  u32x4 c[4];                    // dims 128g .. 128g+127 (block g of the page)
+  u32x2 r;                       // RoPE dims 16g .. 16g+15
+  u32x2 mc;                      // (scale, zero) of groups 2g, 2g+1
+  uint32_t mr;                   // RoPE (scale, zero)
+};
+template <> struct LaneSlot<1> {     // C2R4
+  u32x4 c[2];                    // dims 128g .. 128g+127 (half of block g/2)
+  u32x2 r;
+  u32x2 mc;
+  uint32_t mr;
+};
+
+template <int F>
+__device__ __forceinline__ LaneSlot<F> load_lane_slot(const uint8_t* pg, int tt, int g) {
+  using FM = Fmt<F>;
+  LaneSlot<F> p;
+  if constexpr (F == 0) {
+    const uint8_t* row = pg + (g * PAGE + tt) * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p.c[i] = *(const u32x4*)(row + 16 * i);
+  } else {
+    const uint8_t* row = pg + ((g >> 1) * PAGE + tt) * 64 + 32 * (g & 1);
+    p.c[0] = *(const u32x4*)row;
+    p.c[1] = *(const u32x4*)(row + 16);
+  }
+  p.r = *(const u32x2*)(pg + FM::OFF_R + tt * 32 + 8 * g);
+  p.mc = *(const u32x2*)(pg + FM::OFF_MC + tt * 32 + 8 * g);
+  p.mr = *(const uint32_t*)(pg + FM::OFF_MR + tt * 4);
+  return p;
+}
+
 __device__ __forceinline__ float meta_scale(uint32_t m) { return bf16_bits_to_f32(m & 0xffffu); }
 __device__ __forceinline__ float meta_zero(uint32_t m) { return bf16_bits_to_f32(m >> 16); }
 

@@ -55,6 +55,7 @@ Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits);
 int launch_append(int f, const AppendArgs& a, hipStream_t stream);
 int launch_decode(int f, const DecodeArgs& a, hipStream_t stream);
 int launch_decode128(int f, const DecodeArgs& a, hipStream_t stream);   // H % 128 == 0
+int launch_decode16w(int f, const DecodeArgs& a, hipStream_t stream);   // other H
 int launch_dequant_dump(int f, const uint8_t* pages, int64_t page_id, uint16_t* out,
                         hipStream_t stream);
 
