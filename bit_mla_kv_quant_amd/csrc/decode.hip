@@ -37,34 +37,58 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     return;
   }
   const int64_t base = (int64_t)b * a.nsplit * H + h;     // split jj at base + jj*H
-  float M = -INFINITY;
-  for (int jj = 0; jj < ns; ++jj) M = fmaxf(M, a.ws_ml[(base + (int64_t)jj * H) * 4]);
   f32x4 accv = {0.f, 0.f, 0.f, 0.f};
-  float ssum = 0.f, fsum = 0.f;
-  int jj = 0;
-  for (; jj + 4 <= ns; jj += 4) {
-    f32x4 ml[4], ov[4];
+  float ssum = 0.f, fsum = 0.f, M = -INFINITY;
+  if (ns <= 8) {
+    // every partial in flight at once, then one pass
+    f32x4 ml[8], ov[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t e = base + (int64_t)(jj + u) * H;
-      ml[u] = *(const f32x4*)(a.ws_ml + e * 4);
-      ov[u] = *(const f32x4*)(a.ws_o + e * DC + d0);
+    for (int u = 0; u < 8; ++u) {
+      if (u < ns) {
+        const int64_t e = base + (int64_t)u * H;
+        ml[u] = *(const f32x4*)(a.ws_ml + e * 4);
+        ov[u] = *(const f32x4*)(a.ws_o + e * DC + d0);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float wgt = ml[u][0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[u][0] - M);
-      ssum += wgt * ml[u][1];
-      fsum += wgt * ml[u][2];
-      accv += wgt * ov[u];
+    for (int u = 0; u < 8; ++u)
+      if (u < ns) M = fmaxf(M, ml[u][0]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < ns) {
+        const float wgt = ml[u][0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[u][0] - M);
+        ssum += wgt * ml[u][1];
+        fsum += wgt * ml[u][2];
+        accv += wgt * ov[u];
+      }
     }
-  }
-  for (; jj < ns; ++jj) {
-    const int64_t e = base + (int64_t)jj * H;
-    const f32x4 ml = *(const f32x4*)(a.ws_ml + e * 4);
-    const float wgt = ml[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[0] - M);
-    ssum += wgt * ml[1];
-    fsum += wgt * ml[2];
-    accv += wgt * *(const f32x4*)(a.ws_o + e * DC + d0);
+  } else {
+    for (int jj = 0; jj < ns; ++jj) M = fmaxf(M, a.ws_ml[(base + (int64_t)jj * H) * 4]);
+    int jj = 0;
+    for (; jj + 4 <= ns; jj += 4) {
+      f32x4 ml[4], ov[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t e = base + (int64_t)(jj + u) * H;
+        ml[u] = *(const f32x4*)(a.ws_ml + e * 4);
+        ov[u] = *(const f32x4*)(a.ws_o + e * DC + d0);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wgt = ml[u][0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[u][0] - M);
+        ssum += wgt * ml[u][1];
+        fsum += wgt * ml[u][2];
+        accv += wgt * ov[u];
+      }
+    }
+    for (; jj < ns; ++jj) {
+      const int64_t e = base + (int64_t)jj * H;
+      const f32x4 ml = *(const f32x4*)(a.ws_ml + e * 4);
+      const float wgt = ml[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[0] - M);
+      ssum += wgt * ml[1];
+      fsum += wgt * ml[2];
+      accv += wgt * *(const f32x4*)(a.ws_o + e * DC + d0);
+    }
   }
   *(f32x4*)o = accv * (1.0f / ssum);
   if (blockIdx.x == 0 && c == 0)

@@ -281,6 +281,10 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
     if (wave < nquart) {
       LaneSlot<F> cur = load_quarter(wave);
       for (int q = wave; q < nquart; q += NW) {
+        // the two waves of a SIMD take turns at the higher issue priority, so
+        // neither finishes its quarters far ahead of the other
+        if (((q >> 3) ^ (wave >> 2)) & 1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
         const int phys = page_id(q >> 2);
         const f32x4 sc = ordinary(q, phys, cur) ? quarter(std::true_type{}, q, phys, cur)
                                                 : quarter(std::false_type{}, q, phys, cur);
@@ -288,6 +292,7 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
         aggregate(q, phys, sc);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // a head beyond the headroom: raise its reference, redo this wave's part
     if (!__any(m_need != -INFINITY)) break;
     if (m_need != -INFINITY) m_ref = m_need;
