@@ -144,10 +144,16 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
     const int i0 = (p0 + (q >> 2)) * PAGE + QT * (q & 3);   // first token of the quarter
     uint16_t* rw = vt + n16 * VT_PITCH + 128 * g;
     f32x4 se = {0.f, 0.f, 0.f, 0.f}, so = {0.f, 0.f, 0.f, 0.f};   // even / odd slices
+    // query slices are read QPF slices ahead of their MFMA (LDS latency)
+    constexpr int QPF = 3;
+    bf16x8 qn[QPF];
+#pragma unroll
+    for (int s = 0; s < QPF; ++s) qn[s] = qslice(s);
     auto qk = [&](const int s, const bf16x8 kv) {
-      if (s & 1) so = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qslice(s), so, 0, 0, 0);
-      else se = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qslice(s), se, 0, 0, 0);
-      if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);      // bound the slices in flight
+      const bf16x8 qs = qn[s % QPF];
+      if (s + QPF < 18) qn[s % QPF] = qslice(s + QPF);
+      if (s & 1) so = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qs, so, 0, 0, 0);
+      else se = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qs, se, 0, 0, 0);
     };
     if constexpr (ORDINARY) {
 #pragma unroll
@@ -247,12 +253,19 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
     const bf16x8 pb = bitcast<bf16x8>(pw);
     // O^T[16nb + 4g + v][head] += C^T . P^T over the quarter's 16 tokens
     const uint16_t* va = vt + (4 * g + (n16 >> 2)) * VT_PITCH + 4 * (n16 & 3);
+    // transposed reads run CPF dim tiles ahead of their MFMA (LDS latency)
+    constexpr int CPF = 6;
+    bf16x4 cn[CPF];
+#pragma unroll
+    for (int nb = 0; nb < CPF; ++nb)
+      cn[nb] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va + 16 * nb));
 #pragma unroll
     for (int nb = 0; nb < 32; ++nb) {
-      const bf16x4 c4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va + 16 * nb));
+      const bf16x4 c4 = cn[nb % CPF];
+      if (nb + CPF < 32)
+        cn[nb % CPF] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va + 16 * (nb + CPF)));
       const bf16x8 ct = __builtin_shufflevector(c4, c4, 0, 1, 2, 3, 0, 1, 2, 3);
       acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ct, pb, acc[nb], 0, 0, 0);
-      if ((nb & 7) == 7) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
     }
   };
 
