@@ -184,42 +184,71 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
       qk(17, deq_int4x8_fp8(sl.r[1], s9, z));
     } else {
       // a quarter holding a sink or recent-window token, unusable slots, or
-      // a scale beyond the fp8 path: per-lane substitutions
+      // a scale beyond the fp8 path: per-lane substitutions.  The BF16 rows
+      // of protected tokens are requested in batches before any is used
+      // (one memory latency per batch, not one per slice).
       const int i = i0 + n16;
       const bool valid = phys >= 0 && i < L;
       const bool prot = valid && is_protected(i, L);
       const uint16_t* prow = prot_seq + (int64_t)(prot ? prot_row(i) : 0) * DROW;
-      auto fix = [&](const bf16x8 v, const int off) -> bf16x8 {
-        if (prot) return *(const bf16x8*)(prow + off);
-        return valid ? v : bitcast<bf16x8>(u32x4{0u, 0u, 0u, 0u});
+      auto slice_off = [&](const int s) {            // row offset of slice s
+        return s < 16 ? 128 * g + 8 * s : DC + 16 * g + 8 * (s - 16);
       };
+      auto prot_slice = [&](const int s) -> bf16x8 {
+        return prot ? *(const bf16x8*)(prow + slice_off(s)) : bitcast<bf16x8>(u32x4{0u, 0u, 0u, 0u});
+      };
+      if (__all(prot)) {
+        // a quarter of the recent window: nothing to reconstruct, so slice s
+        // of lane g is dims 32s + 8g (s < 16) or 512 + 32(s-16) + 8g -- the
+        // four lanes of a token read 64 contiguous bytes of its row
+        auto off_p = [&](const int s) { return (s < 16 ? 32 * s : DC + 32 * (s - 16)) + 8 * g; };
+        bf16x8 pr[18];
 #pragma unroll
-      for (int grp = 0; grp < 2; ++grp) {
-        if constexpr (F == 0) {
+        for (int s = 0; s < 18; ++s) pr[s] = *(const bf16x8*)(prow + off_p(s));
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const bf16x8 kv =
-                fix(deq_int4x8(sl.c[2 * grp + (t >> 2)][t & 3], sl.mc[grp]), 128 * g + 64 * grp + 8 * t);
-            qk(8 * grp + t, kv);
-            *(bf16x8*)(rw + 64 * grp + 8 * t) = kv;
-          }
-        } else {
-          const Lut2 lut = make_lut2(meta_scale(sl.mc[grp]), meta_zero(sl.mc[grp]));
+        for (int s = 0; s < 18; ++s) {
+          const bf16x8 qs = *(const bf16x8*)(qrow + off_p(s));
+          if (s & 1) so = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pr[s], qs, so, 0, 0, 0);
+          else se = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pr[s], qs, se, 0, 0, 0);
+          if (s < 16) *(bf16x8*)(vt + n16 * VT_PITCH + off_p(s)) = pr[s];
+        }
+      } else {
+        bf16x8 pr[8];
+        auto fix = [&](const bf16x8 v, const int s) -> bf16x8 {
+          if (prot) return pr[s & 7];
+          return valid ? v : bitcast<bf16x8>(u32x4{0u, 0u, 0u, 0u});
+        };
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            bf16x8 ka, kb;
-            deq_int2x16(sl.c[grp][w], lut, ka, kb);
-            ka = fix(ka, 128 * g + 64 * grp + 16 * w);
-            kb = fix(kb, 128 * g + 64 * grp + 16 * w + 8);
-            qk(8 * grp + 2 * w, ka);
-            qk(8 * grp + 2 * w + 1, kb);
-            *(bf16x8*)(rw + 64 * grp + 16 * w) = ka;
-            *(bf16x8*)(rw + 64 * grp + 16 * w + 8) = kb;
+        for (int grp = 0; grp < 2; ++grp) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) pr[t] = prot_slice(8 * grp + t);
+          if constexpr (F == 0) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              const bf16x8 kv = fix(deq_int4x8(sl.c[2 * grp + (t >> 2)][t & 3], sl.mc[grp]), 8 * grp + t);
+              qk(8 * grp + t, kv);
+              *(bf16x8*)(rw + 64 * grp + 8 * t) = kv;
+            }
+          } else {
+            const Lut2 lut = make_lut2(meta_scale(sl.mc[grp]), meta_zero(sl.mc[grp]));
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              bf16x8 ka, kb;
+              deq_int2x16(sl.c[grp][w], lut, ka, kb);
+              ka = fix(ka, 8 * grp + 2 * w);
+              kb = fix(kb, 8 * grp + 2 * w + 1);
+              qk(8 * grp + 2 * w, ka);
+              qk(8 * grp + 2 * w + 1, kb);
+              *(bf16x8*)(rw + 64 * grp + 16 * w) = ka;
+              *(bf16x8*)(rw + 64 * grp + 16 * w + 8) = kb;
+            }
           }
         }
+        pr[0] = prot_slice(16);
+        pr[1] = prot_slice(17);
+        qk(16, fix(deq_int4x8(sl.r[0], sl.mr), 16));
+        qk(17, fix(deq_int4x8(sl.r[1], sl.mr), 17));
       }
-      qk(16, fix(deq_int4x8(sl.r[0], sl.mr), DC + 16 * g));
-      qk(17, fix(deq_int4x8(sl.r[1], sl.mr), DC + 16 * g + 8));
     }
 
     return se + so;
