@@ -190,6 +190,8 @@ def main():
     ap.add_argument("--config", type=int, default=1, help="synthetic workload id (0-4)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graphs")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="splits per max-length sequence (0: the library's automatic plan)")
     ap.add_argument("--min-rotation-gib", type=float, default=1.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (HBM counter calibration)")
@@ -224,7 +226,7 @@ def main():
     torch.cuda.synchronize()
     log(f"replicas {R} x {fp / 2**20:.1f} MiB")
 
-    ws_bytes = ops.mla_decode_lowbit_workspace(fmt, B, H, max_len, 0)
+    ws_bytes = ops.mla_decode_lowbit_workspace(fmt, B, H, max_len, args.splits)
     for r in reps:
         r["ws"] = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
         r["out"] = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
@@ -239,7 +241,7 @@ def main():
 
     def do_decode(r):
         ops.mla_decode_lowbit(fmt, r["q_lat"], r["q_rope"], r["pages"], r["prot"], r["seq_slot"],
-                              r["block_table"], r["seq_lens"], max_len, d.scale, 0,
+                              r["block_table"], r["seq_lens"], max_len, d.scale, args.splits,
                               workspace=r["ws"] if ws_bytes else None, out=r["out"],
                               lse=r["lse"], stream=stream)
 
