@@ -26,9 +26,11 @@ offsets multiples of 256 bytes:
                                           16 bits apart
   codes_r  [64 tok][32 B]  byte k: RoPE dims 2k (bits 0-3), 2k+1 (bits 4-7)
   meta_c   [64 tok][8 grp][2] bf16 (scale, zero), little endian
-  meta_r   [64 tok][2] bf16 (scale, zero)
+  meta_r   [64 tok][2] bf16 (scale, zero); format C4R4F (content as C4R4):
+           [64 tok][2] fp32 (scale, zero), little endian
 
-  page bytes: C4R4 16384+2048+2048+256 = 20736 ; C2R4 8192+2048+2048+256 = 12544
+  page bytes: C4R4 16384+2048+2048+256 = 20736 ; C2R4 8192+2048+2048+256 = 12544 ;
+              C4R4F 16384+2048+2048+512 = 20992
 
 A slot index is page_id * 64 + offset.
 
@@ -40,7 +42,7 @@ most recent tokens and a new token replaces exactly the one leaving the window.
 
 import numpy as np
 
-from .quant import D_C, D_R, N_GROUPS_C
+from .quant import D_C, D_R, F32_ROPE, FORMATS, N_GROUPS_C
 
 PAGE_TOKENS = 64
 N_SINK = 4
@@ -49,11 +51,11 @@ PROT_ROWS = N_SINK + N_RECENT   # 132
 
 
 def _regions(fmt):
-    cbytes = {"C4R4": 256, "C2R4": 128}[fmt]          # content code bytes per token
+    cbytes = FORMATS[fmt][0] * D_C // 8               # content code bytes per token
     codes_c = PAGE_TOKENS * cbytes
     codes_r = PAGE_TOKENS * 32
     meta_c = PAGE_TOKENS * N_GROUPS_C * 4
-    meta_r = PAGE_TOKENS * 4
+    meta_r = PAGE_TOKENS * (8 if fmt in F32_ROPE else 4)   # (scale, zero) fp32 or bf16
     off_r = codes_c
     off_mc = off_r + codes_r
     off_mr = off_mc + meta_c
@@ -70,7 +72,7 @@ def pack_content(codes_c, fmt):
     """codes_c uint8 [T,512] -> per-token packed content bytes [T, n_blk, 64]."""
     q = np.asarray(codes_c, dtype=np.uint8)
     T = q.shape[0]
-    if fmt == "C4R4":
+    if FORMATS[fmt][0] == 4:
         # blk b covers dims 128b..128b+127; byte k = dims 2k (lo), 2k+1 (hi)
         q = q.reshape(T, 4, 64, 2)
         return (q[..., 0] | (q[..., 1] << 4)).astype(np.uint8)
@@ -86,7 +88,7 @@ def unpack_content(packed, fmt):
     """Inverse of pack_content: [T, n_blk, 64] bytes -> codes [T,512]."""
     p = np.asarray(packed, dtype=np.uint8)
     T = p.shape[0]
-    if fmt == "C4R4":
+    if FORMATS[fmt][0] == 4:
         return np.stack([p & 0xF, p >> 4], axis=-1).reshape(T, D_C).astype(np.uint8)
     words = np.ascontiguousarray(p).view("<u4").reshape(T, 2, 16, 1).astype(np.uint32)
     shift_even = (2 * np.arange(8, dtype=np.uint32))
@@ -129,9 +131,14 @@ def write_tokens(pages, slots, qt, fmt):
         meta = np.stack([qt["scale"][t, :N_GROUPS_C], qt["zero"][t, :N_GROUPS_C]], axis=1)
         base = R["off_mc"] + off * N_GROUPS_C * 4
         page[base:base + N_GROUPS_C * 4] = meta.astype("<u2").reshape(-1).view(np.uint8)
-        mr = np.array([qt["scale"][t, N_GROUPS_C], qt["zero"][t, N_GROUPS_C]], dtype="<u2")
-        base = R["off_mr"] + off * 4
-        page[base:base + 4] = mr.view(np.uint8)
+        if fmt in F32_ROPE:
+            mr = np.array([qt["scale_r32"][t], qt["zero_r32"][t]], dtype="<f4")
+            base = R["off_mr"] + off * 8
+            page[base:base + 8] = mr.view(np.uint8)
+        else:
+            mr = np.array([qt["scale"][t, N_GROUPS_C], qt["zero"][t, N_GROUPS_C]], dtype="<u2")
+            base = R["off_mr"] + off * 4
+            page[base:base + 4] = mr.view(np.uint8)
 
 
 def read_page(page, fmt):
@@ -144,13 +151,17 @@ def read_page(page, fmt):
     pr = page[R["off_r"]:R["off_r"] + PAGE_TOKENS * 32].reshape(PAGE_TOKENS, 32)
     mc = page[R["off_mc"]:R["off_mc"] + PAGE_TOKENS * N_GROUPS_C * 4].copy().view("<u2")
     mc = mc.reshape(PAGE_TOKENS, N_GROUPS_C, 2)
-    mr = page[R["off_mr"]:R["off_mr"] + PAGE_TOKENS * 4].copy().view("<u2").reshape(PAGE_TOKENS, 2)
-    return {
-        "codes_c": unpack_content(pc, fmt),
-        "codes_r": unpack_rope(pr),
-        "scale": np.concatenate([mc[:, :, 0], mr[:, :1]], axis=1).astype(np.uint16),
-        "zero": np.concatenate([mc[:, :, 1], mr[:, 1:]], axis=1).astype(np.uint16),
-    }
+    out = {"codes_c": unpack_content(pc, fmt), "codes_r": unpack_rope(pr)}
+    if fmt in F32_ROPE:
+        mr32 = page[R["off_mr"]:R["off_mr"] + PAGE_TOKENS * 8].copy().view("<f4").reshape(PAGE_TOKENS, 2)
+        out["scale_r32"] = mr32[:, 0].astype(np.float32)
+        out["zero_r32"] = mr32[:, 1].astype(np.float32)
+        mr = np.zeros((PAGE_TOKENS, 2), np.uint16)
+    else:
+        mr = page[R["off_mr"]:R["off_mr"] + PAGE_TOKENS * 4].copy().view("<u2").reshape(PAGE_TOKENS, 2)
+    out["scale"] = np.concatenate([mc[:, :, 0], mr[:, :1]], axis=1).astype(np.uint16)
+    out["zero"] = np.concatenate([mc[:, :, 1], mr[:, 1:]], axis=1).astype(np.uint16)
+    return out
 
 
 def prot_row(i):

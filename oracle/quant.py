@@ -23,9 +23,18 @@ q*s is exact in fp32 (<= 8-bit integer times an 8-bit-mantissa scale), so a
 fused multiply-add and a multiply followed by an add round identically.
 
 Metadata dtype: [QuantMLA App. C.4/C.5] store content scales in BF16 and RoPE
-scales in FP32; the format built here stores (scale, zero) in bf16 for all
-nine groups (content and RoPE alike).  The FP32-RoPE variant is a separate,
-not-yet-built format.
+scales in FP32.  Formats C4R4 and C2R4 store (scale, zero) in bf16 for all
+nine groups (content and RoPE alike).  Format C4R4F follows the pages' split:
+content groups as in C4R4, the RoPE group's scale and zero in fp32:
+
+    s  = fl32( fl32(hi - lo) / m )                 stored scale (fp32)
+    z  = lo                                        stored zero (fp32, exact)
+    q  = clamp( rint_even( fl32( fl32(x - z) / s ) ), 0, m )   if s > 0
+    x^ = bf16_rne( fl32( fl32(q * s) + z ) )       reconstructed bf16 value
+
+With an fp32 scale q*s can need more than 24 significant bits, so the
+product is rounded to fp32 before the zero is added (two IEEE roundings, the
+plain reading of "dequantize with the stored scale" in fp32 arithmetic).
 
 All arrays of bf16 values are carried as uint16 bit patterns.
 """
@@ -40,7 +49,9 @@ N_GROUPS_C = D_C // GROUP   # 8
 N_GROUPS = N_GROUPS_C + 1   # 9 (8 content + 1 RoPE)
 
 # format name -> (content bits, rope bits)   [QuantMLA §4.1]
-FORMATS = {"C4R4": (4, 4), "C2R4": (2, 4)}
+FORMATS = {"C4R4": (4, 4), "C2R4": (2, 4), "C4R4F": (4, 4)}
+# formats whose RoPE group keeps its (scale, zero) in fp32 [QuantMLA App. C.4/C.5]
+F32_ROPE = frozenset({"C4R4F"})
 
 
 # ---------------------------------------------------------------- bf16 -----
@@ -97,6 +108,40 @@ def quantize_groups(x_bits, bits):
     return q, s_bits, z_bits
 
 
+def quantize_groups_f32meta(x_bits, bits):
+    """Quantize groups of 64 bf16 values keeping (scale, zero) in fp32.
+
+    returns (codes uint8 [..., 64], scale float32 [...], zero float32 [...]).
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    assert x_bits.shape[-1] == GROUP
+    m = np.float32((1 << bits) - 1)
+    x = bf16_to_f32(x_bits)
+    lo = x.min(axis=-1)
+    hi = x.max(axis=-1)
+    rng = (hi - lo).astype(np.float32)                    # fl32(hi - lo)
+    s = (rng / m).astype(np.float32)                      # fl32(rng / m), kept in fp32
+    z = lo.astype(np.float32)
+    pos = s > 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        d = (x - z[..., None]).astype(np.float32)         # fl32(x - z)
+        t = (d / s[..., None]).astype(np.float32)         # fl32(d / s)
+    q = np.rint(t)                                        # ties to even
+    q = np.clip(q, 0, m)
+    q = np.where(pos[..., None], q, 0).astype(np.uint8)
+    return q, s, z
+
+
+def dequantize_groups_f32meta(codes, scale, zero):
+    """x^ = bf16(fl32(fl32(q * s) + z)) with fp32 (s, z): [..., 64] -> uint16 [..., 64]."""
+    q = np.asarray(codes).astype(np.float32)
+    s = np.asarray(scale, dtype=np.float32)[..., None]
+    z = np.asarray(zero, dtype=np.float32)[..., None]
+    y = (q * s).astype(np.float32)      # one fp32 rounding of the product
+    y = (y + z).astype(np.float32)      # one fp32 rounding of the sum
+    return f32_to_bf16(y)
+
+
 def dequantize_groups(codes, scale_bits, zero_bits):
     """x^ = bf16(fl32(q * s + z)); codes [..., 64], scale/zero [...] -> uint16 [..., 64]."""
     q = np.asarray(codes).astype(np.float32)
@@ -113,19 +158,27 @@ def quantize_tokens(c_bits, kr_bits, fmt):
     returns dict with
       codes_c uint8 [T,512], codes_r uint8 [T,64],
       scale uint16 [T,9], zero uint16 [T,9]   (groups 0..7 content, 8 RoPE)
+    and, for formats in F32_ROPE, the RoPE group's fp32 metadata
+      scale_r32 float32 [T], zero_r32 float32 [T]   (column 8 of scale/zero is 0)
     """
     bc, br = FORMATS[fmt]
     c_bits = np.asarray(c_bits, dtype=np.uint16)
     kr_bits = np.asarray(kr_bits, dtype=np.uint16)
     T = c_bits.shape[0]
     qc, sc, zc = quantize_groups(c_bits.reshape(T, N_GROUPS_C, GROUP), bc)
-    qr, sr, zr = quantize_groups(kr_bits.reshape(T, 1, GROUP), br)
-    return {
-        "codes_c": qc.reshape(T, D_C),
-        "codes_r": qr.reshape(T, D_R),
-        "scale": np.concatenate([sc, sr], axis=1),
-        "zero": np.concatenate([zc, zr], axis=1),
-    }
+    out = {"codes_c": qc.reshape(T, D_C)}
+    if fmt in F32_ROPE:
+        qr, sr32, zr32 = quantize_groups_f32meta(kr_bits.reshape(T, 1, GROUP), br)
+        sr = np.zeros((T, 1), np.uint16)
+        zr = np.zeros((T, 1), np.uint16)
+        out["scale_r32"] = sr32.reshape(T)
+        out["zero_r32"] = zr32.reshape(T)
+    else:
+        qr, sr, zr = quantize_groups(kr_bits.reshape(T, 1, GROUP), br)
+    out["codes_r"] = qr.reshape(T, D_R)
+    out["scale"] = np.concatenate([sc, sr], axis=1)
+    out["zero"] = np.concatenate([zc, zr], axis=1)
+    return out
 
 
 def dequantize_tokens(qt):
@@ -133,6 +186,10 @@ def dequantize_tokens(qt):
     T = qt["codes_c"].shape[0]
     c = dequantize_groups(qt["codes_c"].reshape(T, N_GROUPS_C, GROUP),
                           qt["scale"][:, :N_GROUPS_C], qt["zero"][:, :N_GROUPS_C])
-    r = dequantize_groups(qt["codes_r"].reshape(T, 1, GROUP),
-                          qt["scale"][:, N_GROUPS_C:], qt["zero"][:, N_GROUPS_C:])
+    if "scale_r32" in qt:
+        r = dequantize_groups_f32meta(qt["codes_r"].reshape(T, 1, GROUP),
+                                      qt["scale_r32"].reshape(T, 1), qt["zero_r32"].reshape(T, 1))
+    else:
+        r = dequantize_groups(qt["codes_r"].reshape(T, 1, GROUP),
+                              qt["scale"][:, N_GROUPS_C:], qt["zero"][:, N_GROUPS_C:])
     return np.concatenate([c.reshape(T, D_C), r.reshape(T, D_R)], axis=1)

@@ -35,6 +35,17 @@ def test_compression_with_library_page():
     assert round(acc.compression(131072, layout.page_bytes("C4R4")), 2) == 3.54
 
 
+def test_compression_with_fp32_rope_metadata_page():
+    # C4R4F: 20,992-byte pages (328 B/token against the pages' 320); by hand,
+    # 4K: 64 * 73,728 / (64 * 21,000 + 152,064) = 4,718,592 / 1,496,064
+    # 128K: 2048 * 73,728 / (2048 * 21,000 + 152,064) = 150,994,944 / 43,160,064
+    assert layout.page_bytes("C4R4F") == 20992
+    assert acc.packed_bytes(4096, 20992) == 1496064
+    assert acc.packed_bytes(131072, 20992) == 43160064
+    assert round(acc.compression(4096, 20992), 2) == 3.15
+    assert round(acc.compression(131072, 20992), 2) == 3.50
+
+
 def test_schema_counts():
     e = GOLD["mha_elements_per_token_layer"]
     assert acc.mha_elements(e["heads"], e["head_dim"]) == e["value"]

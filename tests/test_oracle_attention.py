@@ -44,11 +44,12 @@ def test_protected_set_enumeration():
         assert np.all((rows >= 0) & (rows < 132))
 
 
-def test_effective_rows_mixing():
+@pytest.mark.parametrize("fmt", ["C4R4", "C4R4F"])
+def test_effective_rows_mixing(fmt):
     c, kr, *_ = _seq(300, seed=5)
-    rows = attention.effective_rows(c, kr, "C4R4")
+    rows = attention.effective_rows(c, kr, fmt)
     orig = quant.bf16_to_f32(np.concatenate([c, kr], 1)).astype(np.float64)
-    deq = quant.bf16_to_f32(quant.dequantize_tokens(quant.quantize_tokens(c, kr, "C4R4")))
+    deq = quant.bf16_to_f32(quant.dequantize_tokens(quant.quantize_tokens(c, kr, fmt)))
     for i in (0, 3, 172, 299):
         np.testing.assert_array_equal(rows[i], orig[i])
     for i in (4, 100, 171):
@@ -67,7 +68,8 @@ def test_all_protected_equals_sdpa(L):
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
 
 
-def test_exactly_quantizable_long_sequence_equals_sdpa():
+@pytest.mark.parametrize("fmt", ["C4R4", "C4R4F"])
+def test_exactly_quantizable_long_sequence_equals_sdpa(fmt):
     """Rows built on each group's code grid survive quantization unchanged, so
     for any L the mixed-precision result equals plain attention."""
     rng = np.random.default_rng(7)
@@ -80,11 +82,11 @@ def test_exactly_quantizable_long_sequence_equals_sdpa():
     xb = quant.f32_to_bf16(x)
     assert np.array_equal(quant.bf16_to_f32(xb), x)
     c, kr = xb[:, :512], xb[:, 512:]
-    rows = attention.effective_rows(c, kr, "C4R4")
+    rows = attention.effective_rows(c, kr, fmt)
     np.testing.assert_array_equal(rows, x.astype(np.float64))
     ql = quant.f32_to_bf16(rng.normal(0, 0.07, (H, 512)).astype(np.float32))
     qr = quant.f32_to_bf16(rng.normal(0, 0.07, (H, 64)).astype(np.float32))
-    out, _ = attention.decode_sequence(c, kr, ql, qr, "C4R4", 0.1)
+    out, _ = attention.decode_sequence(c, kr, ql, qr, fmt, 0.1)
     q = quant.bf16_to_f32(np.concatenate([ql, qr], 1))
     ref = _sdpa(q, x, x[:, :512], 0.1)
     np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)

@@ -154,6 +154,110 @@ def test_dequant_is_one_fp32_rounding_then_bf16():
             assert Fraction(float(got[g, j])) == want
 
 
+# ----------------------------------------- fp32 RoPE metadata (C4R4F) ---
+def _rint_even(fr):
+    lo = fr.numerator // fr.denominator
+    rem = fr - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return lo
+
+
+def test_quantizer_f32meta_follows_stated_steps_and_is_nearest():
+    """fp32 (scale, zero) [QuantMLA App. C.4/C.5]: s = fl32(fl32(hi-lo)/m),
+    z = lo, q = clamp(rint(fl32(fl32(x-z)/s))), replayed step by step in exact
+    rational arithmetic; every code is also the nearest reconstruction point
+    up to the fp32 rounding of the quotient."""
+    rng = np.random.default_rng(31)
+    xb = np.concatenate([_groups_small_int(rng, 200),
+                         quant.f32_to_bf16((rng.standard_normal((200, 64)) * 3).astype(np.float32))])
+    q, s32, z32 = quant.quantize_groups_f32meta(xb, 4)
+    assert s32.dtype == np.float32 and z32.dtype == np.float32
+    m = 15
+    xf = quant.bf16_to_f32(xb)
+    for g in range(xb.shape[0]):
+        lo, hi = Fraction(float(xf[g].min())), Fraction(float(xf[g].max()))
+        s = _exact_round_to_bits(_exact_round_to_bits(hi - lo, 24) / m, 24) if hi != lo else Fraction(0)
+        assert Fraction(float(s32[g])) == s and Fraction(float(z32[g])) == lo
+        for j in range(64):
+            x = Fraction(float(xf[g, j]))
+            if s == 0:
+                assert q[g, j] == 0
+                continue
+            t = _exact_round_to_bits(_exact_round_to_bits(x - lo, 24) / s, 24)
+            assert q[g, j] == min(max(_rint_even(t), 0), m), (g, j)
+            d = [abs(x - (k * s + lo)) for k in range(m + 1)]
+            assert d[q[g, j]] <= min(d) + s * Fraction(1, 1 << 20), (g, j)
+
+
+def test_dequant_f32meta_rounds_product_then_sum():
+    """x^ = bf16(fl32(fl32(q*s) + z)): checked against exact rationals, and
+    the two roundings differ from a single fused rounding on some inputs."""
+    rng = np.random.default_rng(32)
+    xb = quant.f32_to_bf16((rng.standard_normal((300, 64)) * 7 + 3).astype(np.float32))
+    q, s32, z32 = quant.quantize_groups_f32meta(xb, 4)
+    got = quant.bf16_to_f32(quant.dequantize_groups_f32meta(q, s32, z32))
+    fused_differs = 0
+    for g in range(300):
+        s, z = Fraction(float(s32[g])), Fraction(float(z32[g]))
+        for j in range(64):
+            p = int(q[g, j]) * s
+            want = _exact_round_to_bits(_exact_round_to_bits(_exact_round_to_bits(p, 24) + z, 24), 8)
+            assert Fraction(float(got[g, j])) == want
+            fused = _exact_round_to_bits(p + z, 24)
+            fused_differs += fused != _exact_round_to_bits(_exact_round_to_bits(p, 24) + z, 24)
+    assert fused_differs > 0      # the reading of the two roundings matters
+
+
+def test_quantizer_f32meta_bound_and_exact_minimum():
+    rng = np.random.default_rng(33)
+    xb = quant.f32_to_bf16((rng.standard_normal((4000, 64)) * 2.5).astype(np.float32))
+    q, s32, z32 = quant.quantize_groups_f32meta(xb, 4)
+    x = quant.bf16_to_f32(xb).astype(np.float64)
+    s = s32.astype(np.float64)
+    recon = q * s[:, None] + z32.astype(np.float64)[:, None]
+    assert np.all(np.abs(x - recon) <= 0.5 * s[:, None] * (1 + 1e-6))
+    amin = x.argmin(axis=1)
+    xh = quant.bf16_to_f32(quant.dequantize_groups_f32meta(q, s32, z32))
+    assert np.all(xh[np.arange(len(q)), amin] == x[np.arange(len(q)), amin])
+    # a constant group: s = 0, every code 0, exact reconstruction
+    cb = quant.f32_to_bf16(np.full((2, 64), [[2.5], [-1.0]], dtype=np.float32))
+    qc, sc, zc = quant.quantize_groups_f32meta(cb, 4)
+    assert np.all(qc == 0) and np.all(sc == 0)
+    np.testing.assert_array_equal(quant.dequantize_groups_f32meta(qc, sc, zc), cb)
+
+
+def test_c4r4f_tokens_keep_content_as_c4r4():
+    rng = np.random.default_rng(34)
+    c = quant.f32_to_bf16(rng.standard_normal((16, 512)).astype(np.float32))
+    kr = quant.f32_to_bf16(rng.standard_normal((16, 64)).astype(np.float32))
+    a, b = quant.quantize_tokens(c, kr, "C4R4"), quant.quantize_tokens(c, kr, "C4R4F")
+    np.testing.assert_array_equal(a["codes_c"], b["codes_c"])
+    np.testing.assert_array_equal(a["scale"][:, :8], b["scale"][:, :8])
+    np.testing.assert_array_equal(a["zero"][:, :8], b["zero"][:, :8])
+    ra = quant.dequantize_tokens(a)
+    rb = quant.dequantize_tokens(b)
+    np.testing.assert_array_equal(ra[:, :512], rb[:, :512])
+    # the RoPE rows agree with the fp32-metadata group routines
+    q, s32, z32 = quant.quantize_groups_f32meta(kr, 4)
+    np.testing.assert_array_equal(b["codes_r"], q)
+    np.testing.assert_array_equal(rb[:, 512:], quant.dequantize_groups_f32meta(q, s32, z32))
+
+
+def test_c4r4f_meta_bytes_known_answer():
+    """RoPE dims 0..63 as values 0..63: s = fl32(63/15) = 4.2f, z = 0, stored
+    little-endian fp32 at the slot's 8-byte meta_r entry."""
+    import struct
+    c = quant.f32_to_bf16(np.zeros((1, 512), np.float32))
+    kr = quant.f32_to_bf16(np.arange(64, dtype=np.float32)[None, :])
+    qt = quant.quantize_tokens(c, kr, "C4R4F")
+    pages = np.zeros((1, layout.page_bytes("C4R4F")), np.uint8)
+    layout.write_tokens(pages, np.array([5]), qt, "C4R4F")
+    off = 16384 + 2048 + 2048 + 5 * 8
+    assert bytes(pages[0, off:off + 8]) == struct.pack("<ff", np.float32(63.0) / np.float32(15.0), 0.0)
+    assert bytes(pages[0, off:off + 8]).hex() == "6666864000000000"
+
+
 # --------------------------------------------------------------- packing ---
 def test_pack_known_answer_c4():
     codes = np.tile(np.arange(16, dtype=np.uint8), 32)[None, :]      # [1, 512]
@@ -186,7 +290,7 @@ def test_pack_known_answer_c2():
     assert p[0, 0, 4 * 3 + 1] == 0x80 and int(p.sum()) == 0x80
 
 
-@pytest.mark.parametrize("fmt", ["C4R4", "C2R4"])
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "C4R4F"])
 def test_pack_roundtrip_and_page_roundtrip(fmt):
     rng = np.random.default_rng(4)
     T = 64
@@ -203,7 +307,10 @@ def test_pack_roundtrip_and_page_roundtrip(fmt):
     assert not pages[:2].any()
     back = layout.read_page(pages[2], fmt)
     inv = np.argsort(slots - 128)
-    for k in ("codes_c", "codes_r", "scale", "zero"):
+    keys = ("codes_c", "codes_r", "scale", "zero")
+    if fmt in quant.F32_ROPE:
+        keys += ("scale_r32", "zero_r32")
+    for k in keys:
         np.testing.assert_array_equal(back[k][slots - 128], qt[k])
     del inv
 
@@ -211,4 +318,5 @@ def test_pack_roundtrip_and_page_roundtrip(fmt):
 def test_page_sizes():
     assert layout.page_bytes("C4R4") == 20736
     assert layout.page_bytes("C2R4") == 12544
+    assert layout.page_bytes("C4R4F") == 20992       # 328 B/token against the pages' 320
     assert layout.PROT_ROWS * 576 * 2 == 152064
