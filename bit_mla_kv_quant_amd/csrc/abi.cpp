@@ -15,7 +15,7 @@ static constexpr int kMinPagesPerSplit = 2;
 static constexpr int kMinPagesPerSplit128 = 8;   // 128-head blocks write 256 KB per split
 
 static size_t page_bytes_of(int f) {
-  return f == MLA_LB_C4R4 ? 20736u : (f == MLA_LB_C2R4 ? 12544u : 0u);
+  return f == MLA_LB_C4R4 ? 20736u : (f == MLA_LB_C2R4 ? 12544u : (f == MLA_LB_C4R4F ? 20992u : 0u));
 }
 
 // Split plan.  A max-length sequence of P pages is cut into nsplit splits of
@@ -76,7 +76,7 @@ int kv_quant_append(int f, const uint16_t* latent, const uint16_t* k_rope,
                     const int64_t* slot_mapping, const int32_t* seq_slot, const int32_t* pos,
                     const int32_t* new_len, int32_t T, uint8_t* pages, int64_t num_pages,
                     uint16_t* prot, int32_t num_seq_slots, void* stream) {
-  if (f != MLA_LB_C4R4 && f != MLA_LB_C2R4) return MLA_LB_EFORMAT;
+  if (mlb::page_bytes_of(f) == 0) return MLA_LB_EFORMAT;
   if (T < 0) return MLA_LB_ESHAPE;
   if (T == 0) return MLA_LB_OK;
   if (!latent || !k_rope || !slot_mapping || !seq_slot || !pos || !new_len || !pages || !prot)
@@ -90,7 +90,7 @@ int kv_quant_append(int f, const uint16_t* latent, const uint16_t* k_rope,
 
 int mla_decode_lowbit_workspace(int f, int32_t B, int32_t H, int32_t max_seq_len,
                                 int32_t num_splits, size_t* bytes) {
-  if (f != MLA_LB_C4R4 && f != MLA_LB_C2R4) return MLA_LB_EFORMAT;
+  if (mlb::page_bytes_of(f) == 0) return MLA_LB_EFORMAT;
   if (!bytes) return MLA_LB_EINVAL;
   if (B < 1 || H < 16 || H > MLA_LB_MAX_HEADS || H % 16 != 0 || max_seq_len < 0 ||
       num_splits < 0)
@@ -106,7 +106,7 @@ int mla_decode_lowbit(int f, const uint16_t* q_lat, const uint16_t* q_rope,
                       const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t H,
                       float softmax_scale, int32_t num_splits, void* workspace,
                       size_t workspace_bytes, float* out, float* lse, void* stream) {
-  if (f != MLA_LB_C4R4 && f != MLA_LB_C2R4) return MLA_LB_EFORMAT;
+  if (mlb::page_bytes_of(f) == 0) return MLA_LB_EFORMAT;
   if (!q_lat || !q_rope || !pages || !prot || !seq_slot || !block_table || !seq_lens || !out ||
       !lse)
     return MLA_LB_EINVAL;
@@ -148,7 +148,7 @@ int mla_decode_lowbit(int f, const uint16_t* q_lat, const uint16_t* q_rope,
 
 int mla_lb_dequant_dump(int f, const uint8_t* pages, int64_t num_pages, int64_t page_id,
                         uint16_t* out, void* stream) {
-  if (f != MLA_LB_C4R4 && f != MLA_LB_C2R4) return MLA_LB_EFORMAT;
+  if (mlb::page_bytes_of(f) == 0) return MLA_LB_EFORMAT;
   if (!pages || !out) return MLA_LB_EINVAL;
   if (num_pages < 1 || page_id < 0 || page_id >= num_pages) return MLA_LB_ESHAPE;
   return mlb::launch_dequant_dump(f, pages, page_id, out, static_cast<hipStream_t>(stream));

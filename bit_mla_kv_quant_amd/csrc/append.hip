@@ -50,6 +50,21 @@ __device__ __forceinline__ uint32_t quantize_lane(float x, int bits, uint32_t& s
   return (uint32_t)q;
 }
 
+// The same with the group's (scale, zero) kept in fp32 (the RoPE group of
+// format C4R4F [QuantMLA App. C.4/C.5]): s = fl32(fl32(hi - lo) / m), z = lo.
+__device__ __forceinline__ uint32_t quantize_lane_f32(float x, int bits, float& s, float& z) {
+  const float m = (float)((1 << bits) - 1);
+  const float lo = wave_min(x);
+  const float hi = wave_max(x);
+  s = (hi - lo) / m;                              // fl32(fl32(hi - lo) / m)
+  z = lo;
+  if (!(s > 0.0f)) return 0u;                     // constant group: all codes 0
+  const float t = (x - lo) / s;                   // fl32(fl32(x - z) / s)
+  float q = rintf(t);                             // ties to even
+  q = fminf(fmaxf(q, 0.0f), m);
+  return (uint32_t)q;
+}
+
 template <int F>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   using FM = Fmt<F>;
@@ -97,7 +112,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     if (lane == 0) *(uint32_t*)(pg + FM::OFF_MC + off * 32 + g * 4) = sb | (zb << 16);
   }
   // ---- RoPE group (always 4 bits)
-  {
+  if constexpr (FM::F32R) {
+    float s32, z32;
+    const uint32_t q = quantize_lane_f32(bf16_bits_to_f32(xr), 4, s32, z32);
+    const uint32_t w = or_reduce(q << (4 * (lane & 7)), 8);
+    if ((lane & 7) == 0) *(uint32_t*)(pg + FM::OFF_R + off * 32 + (lane / 8) * 4) = w;
+    if (lane == 0)
+      *(u32x2*)(pg + FM::OFF_MR + off * 8) = u32x2{__float_as_uint(s32), __float_as_uint(z32)};
+  } else {
     uint32_t sb, zb;
     const uint32_t q = quantize_lane(bf16_bits_to_f32(xr), 4, sb, zb);
     const uint32_t w = or_reduce(q << (4 * (lane & 7)), 8);
@@ -117,8 +139,10 @@ int launch_append(int f, const AppendArgs& a, hipStream_t stream) {
   const dim3 grid((a.T + 3) / 4), block(256);
   if (f == 0)
     hipLaunchKernelGGL(append_kernel<0>, grid, block, 0, stream, a);
-  else
+  else if (f == 1)
     hipLaunchKernelGGL(append_kernel<1>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(append_kernel<2>, grid, block, 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

@@ -24,16 +24,25 @@ constexpr int PROT_ROWS = NSINK + NRECENT;
 constexpr int NGC = DC / 64;    // content groups of 64 per token
 
 // Page geometry per format (byte offsets of the structure-of-arrays regions).
-// C4R4: codes_c [4][64][64] | codes_r [64][32] | meta_c [64][8][2]bf16 | meta_r [64][2]bf16
-// C2R4: codes_c [2][64][64] | ...
+// C4R4:  codes_c [4][64][64] | codes_r [64][32] | meta_c [64][8][2]bf16 | meta_r [64][2]bf16
+// C2R4:  codes_c [2][64][64] | ...
+// C4R4F: as C4R4, but meta_r [64][2]fp32 (the RoPE group's scale and zero in
+//        fp32 [QuantMLA App. C.4/C.5])
 template <int F> struct Fmt;
 template <> struct Fmt<0> {
   static constexpr int CBITS = 4, NBLK = 4, DPB = 128;   // content dims per block
   static constexpr int OFF_R = 16384, OFF_MC = 18432, OFF_MR = 20480, PAGE_BYTES = 20736;
+  static constexpr bool F32R = false;                    // RoPE metadata in fp32
 };
 template <> struct Fmt<1> {
   static constexpr int CBITS = 2, NBLK = 2, DPB = 256;
   static constexpr int OFF_R = 8192, OFF_MC = 10240, OFF_MR = 12288, PAGE_BYTES = 12544;
+  static constexpr bool F32R = false;
+};
+template <> struct Fmt<2> {
+  static constexpr int CBITS = 4, NBLK = 4, DPB = 128;
+  static constexpr int OFF_R = 16384, OFF_MC = 18432, OFF_MR = 20480, PAGE_BYTES = 20992;
+  static constexpr bool F32R = true;
 };
 
 // Protection-buffer row of position i: sinks keep rows 0..3, the recent

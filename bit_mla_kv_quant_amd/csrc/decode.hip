@@ -130,8 +130,10 @@ int launch_dequant_dump(int f, const uint8_t* pages, int64_t page_id, uint16_t* 
                         hipStream_t stream) {
   if (f == 0)
     hipLaunchKernelGGL(dequant_dump_kernel<0>, dim3(1), dim3(512), 0, stream, pages, page_id, out);
-  else
+  else if (f == 1)
     hipLaunchKernelGGL(dequant_dump_kernel<1>, dim3(1), dim3(512), 0, stream, pages, page_id, out);
+  else
+    hipLaunchKernelGGL(dequant_dump_kernel<2>, dim3(1), dim3(512), 0, stream, pages, page_id, out);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

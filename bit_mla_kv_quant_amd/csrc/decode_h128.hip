@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
     if constexpr (ORDINARY) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        if constexpr (F == 0) {
+        if constexpr (Fmt<F>::CBITS == 4) {
           const float s9 = meta_scale(cur.mc[q]) * 512.0f, z = meta_zero(cur.mc[q]);
 #pragma unroll
           for (int t = 0; t < 8; ++t)
@@ -145,8 +145,8 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
         }
       }
       const float s9r = meta_scale(cur.mr) * 512.0f, zr = meta_zero(cur.mr);
-      *(bf16x8*)rr = deq_int4x8_fp8(cur.r[0], s9r, zr);
-      *(bf16x8*)(rr + 8) = deq_int4x8_fp8(cur.r[1], s9r, zr);
+      *(bf16x8*)rr = deq_rope8_fp8<F>(cur.r[0], s9r, zr);
+      *(bf16x8*)(rr + 8) = deq_rope8_fp8<F>(cur.r[1], s9r, zr);
     } else {
       // a page holding a sink or recent-window token, unusable slots, or a
       // scale beyond the fp8 path: per-lane substitutions, slice by slice
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
       };
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        if constexpr (F == 0) {
+        if constexpr (Fmt<F>::CBITS == 4) {
 #pragma unroll
           for (int t = 0; t < 8; ++t)
             *(bf16x8*)(rc + 64 * q + 8 * t) =
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
     const int p = p0 + k;
     if (phys < 0 || p * PAGE < NSINK || (p + 1) * PAGE > L - NRECENT) return false;
     bool fits = meta_scale(cur.mr) * 512.0f <= FP8_PATH_MAX_SCALE9;
-    if constexpr (F == 0)
+    if constexpr (Fmt<F>::CBITS == 4)
       fits = fits && meta_scale(cur.mc[0]) * 512.0f <= FP8_PATH_MAX_SCALE9 &&
              meta_scale(cur.mc[1]) * 512.0f <= FP8_PATH_MAX_SCALE9;
     return !__any(!fits);
@@ -331,8 +331,10 @@ int launch_decode128(int f, const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.nsplit, a.B, a.H / HB), block(256);
   if (f == 0)
     hipLaunchKernelGGL(decode128_kernel<0>, grid, block, 0, stream, a);
-  else
+  else if (f == 1)
     hipLaunchKernelGGL(decode128_kernel<1>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode128_kernel<2>, grid, block, 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
     if constexpr (ORDINARY) {
 #pragma unroll
       for (int grp = 0; grp < 2; ++grp) {
-        if constexpr (F == 0) {
+        if constexpr (Fmt<F>::CBITS == 4) {
           const float s9 = meta_scale(sl.mc[grp]) * 512.0f, z = meta_zero(sl.mc[grp]);
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
@@ -180,8 +180,8 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
         }
       }
       const float s9 = meta_scale(sl.mr) * 512.0f, z = meta_zero(sl.mr);
-      qk(16, deq_int4x8_fp8(sl.r[0], s9, z));
-      qk(17, deq_int4x8_fp8(sl.r[1], s9, z));
+      qk(16, deq_rope8_fp8<F>(sl.r[0], s9, z));
+      qk(17, deq_rope8_fp8<F>(sl.r[1], s9, z));
     } else {
       // a quarter holding a sink or recent-window token, unusable slots, or
       // a scale beyond the fp8 path: per-lane substitutions.  The BF16 rows
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
         for (int grp = 0; grp < 2; ++grp) {
 #pragma unroll
           for (int t = 0; t < 8; ++t) pr[t] = prot_slice(8 * grp + t);
-          if constexpr (F == 0) {
+          if constexpr (Fmt<F>::CBITS == 4) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
               const bf16x8 kv = fix(deq_int4x8(sl.c[2 * grp + (t >> 2)][t & 3], sl.mc[grp]), 8 * grp + t);
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
     const int i0 = (p0 + (q >> 2)) * PAGE + QT * (q & 3);
     if (phys < 0 || i0 < NSINK || i0 + QT > L - NRECENT) return false;
     bool fits = meta_scale(sl.mr) * 512.0f <= FP8_PATH_MAX_SCALE9;
-    if constexpr (F == 0)
+    if constexpr (Fmt<F>::CBITS == 4)
       fits = fits && meta_scale(sl.mc[0]) * 512.0f <= FP8_PATH_MAX_SCALE9 &&
              meta_scale(sl.mc[1]) * 512.0f <= FP8_PATH_MAX_SCALE9;
     return !__any(!fits);
@@ -404,8 +404,10 @@ int launch_decode16w(int f, const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.nsplit, a.B, a.H / 16), block(512);
   if (f == 0)
     hipLaunchKernelGGL(decode16w_kernel<0>, grid, block, 0, stream, a);
-  else
+  else if (f == 1)
     hipLaunchKernelGGL(decode16w_kernel<1>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode16w_kernel<2>, grid, block, 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

@@ -6,6 +6,9 @@
 //     x^ = bf16_rne( fl32(q * s + z) )
 // q * s is exact in fp32 (q < 16, s has an 8-bit significand), so one fused
 // multiply-add rounds exactly once, like the unfused product-then-sum.
+// With an fp32 (scale, zero) pair (the RoPE group of format C4R4F) q * s is
+// not exact, and the reconstruction rounds the product, then the sum:
+//     x^ = bf16_rne( fl32( fl32(q * s) + z ) )
 //
 // Lane geometry: a lane owns one token slot `tt` of a page and, in dim half
 // dh (0 or 1), lane group g (0..3): the 64 content dims 256*dh + 64*g ..+63
@@ -62,6 +65,38 @@ __device__ __forceinline__ bf16x8 deq_int4x8_fp8(uint32_t w, float s9, float z) 
   return bitcast<bf16x8>(r);
 }
 
+// The same 8 codes with an fp32 (scale, zero) pair: the product is rounded
+// to fp32 before the zero is added.  (b * 2^-9) * s9 is one rounding of
+// b * s, so the fp8 conversion still applies.
+__device__ __forceinline__ float mul_then_add(float a, float b, float c) {
+#pragma clang fp contract(off)
+  const float p = a * b;
+  return p + c;
+}
+__device__ __forceinline__ bf16x8 deq_int4x8_fp8_ma(uint32_t w, float s9, float z) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;                  // dims 0,2,4,6
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;           // dims 1,3,5,7
+  const f32x2_t l01 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+  const f32x2_t l23 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+  const f32x2_t h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+  const f32x2_t h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+  u32x4 r;
+  r[0] = pack_bf16x2(mul_then_add(l01[0], s9, z), mul_then_add(h01[0], s9, z));
+  r[1] = pack_bf16x2(mul_then_add(l01[1], s9, z), mul_then_add(h01[1], s9, z));
+  r[2] = pack_bf16x2(mul_then_add(l23[0], s9, z), mul_then_add(h23[0], s9, z));
+  r[3] = pack_bf16x2(mul_then_add(l23[1], s9, z), mul_then_add(h23[1], s9, z));
+  return bitcast<bf16x8>(r);
+}
+__device__ __forceinline__ bf16x8 deq_int4x8_ubyte_ma(uint32_t w, float s, float z) {
+  const uint32_t lo = opaque(w & 0x0F0F0F0Fu);
+  const uint32_t hi = opaque((w >> 4) & 0x0F0F0F0Fu);
+  u32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    r[k] = pack_bf16x2(mul_then_add(ubyte(lo, k), s, z), mul_then_add(ubyte(hi, k), s, z));
+  return bitcast<bf16x8>(r);
+}
+
 // INT2 groups have four possible reconstructions; they are computed once per
 // group with the same arithmetic as above and kept as a byte-permute table:
 // bytes 0-3 = (x^(0), x^(1)) in `lo`, bytes 4-7 = (x^(2), x^(3)) in `hi`.
@@ -109,12 +144,18 @@ template <> struct Packed<1> {   // C2R4
   uint32_t rc;
   uint32_t mr;
 };
+template <> struct Packed<2> {   // C4R4F
+  u32x4 c[2];
+  uint32_t mc;
+  uint32_t rc;
+  u32x2 mr;                      // RoPE (scale, zero) fp32 bit patterns
+};
 
 template <int F>
 __device__ __forceinline__ Packed<F> load_packed(const uint8_t* pg, int tt, int dh, int g) {
   using FM = Fmt<F>;
   Packed<F> p;
-  if constexpr (F == 0) {
+  if constexpr (FM::CBITS == 4) {
     // blocks of 128 dims: block 2dh + g/2, bytes 32*(g&1) .. +31 of the row
     const uint8_t* row = pg + ((2 * dh + (g >> 1)) * PAGE + tt) * 64 + 32 * (g & 1);
     p.c[0] = *(const u32x4*)row;
@@ -125,7 +166,8 @@ __device__ __forceinline__ Packed<F> load_packed(const uint8_t* pg, int tt, int 
   }
   p.mc = *(const uint32_t*)(pg + FM::OFF_MC + tt * 32 + (4 * dh + g) * 4);
   p.rc = *(const uint32_t*)(pg + FM::OFF_R + tt * 32 + 16 * dh + 4 * g);
-  p.mr = *(const uint32_t*)(pg + FM::OFF_MR + tt * 4);
+  if constexpr (FM::F32R) p.mr = *(const u32x2*)(pg + FM::OFF_MR + tt * 8);
+  else p.mr = *(const uint32_t*)(pg + FM::OFF_MR + tt * 4);
   return p;
 }
 
@@ -145,12 +187,18 @@ template <> struct LaneSlot<1> {     // C2R4
   u32x2 mc;
   uint32_t mr;
 };
+template <> struct LaneSlot<2> {     // C4R4F
+  u32x4 c[4];
+  u32x2 r;
+  u32x2 mc;
+  u32x2 mr;                      // RoPE (scale, zero) fp32 bit patterns
+};
 
 template <int F>
 __device__ __forceinline__ LaneSlot<F> load_lane_slot(const uint8_t* pg, int tt, int g) {
   using FM = Fmt<F>;
   LaneSlot<F> p;
-  if constexpr (F == 0) {
+  if constexpr (FM::CBITS == 4) {
     const uint8_t* row = pg + (g * PAGE + tt) * 64;
 #pragma unroll
     for (int i = 0; i < 4; ++i) p.c[i] = *(const u32x4*)(row + 16 * i);
@@ -161,12 +209,16 @@ __device__ __forceinline__ LaneSlot<F> load_lane_slot(const uint8_t* pg, int tt,
   }
   p.r = *(const u32x2*)(pg + FM::OFF_R + tt * 32 + 8 * g);
   p.mc = *(const u32x2*)(pg + FM::OFF_MC + tt * 32 + 8 * g);
-  p.mr = *(const uint32_t*)(pg + FM::OFF_MR + tt * 4);
+  if constexpr (FM::F32R) p.mr = *(const u32x2*)(pg + FM::OFF_MR + tt * 8);
+  else p.mr = *(const uint32_t*)(pg + FM::OFF_MR + tt * 4);
   return p;
 }
 
+// (scale, zero) of a group: a bf16 pair in one word, or fp32 bit patterns
 __device__ __forceinline__ float meta_scale(uint32_t m) { return bf16_bits_to_f32(m & 0xffffu); }
 __device__ __forceinline__ float meta_zero(uint32_t m) { return bf16_bits_to_f32(m >> 16); }
+__device__ __forceinline__ float meta_scale(u32x2 m) { return __uint_as_float(m[0]); }
+__device__ __forceinline__ float meta_zero(u32x2 m) { return __uint_as_float(m[1]); }
 
 // 8 INT4 codes with the fp8 conversion when the scale allows it.
 __device__ __forceinline__ bf16x8 deq_int4x8(uint32_t w, uint32_t meta) {
@@ -175,11 +227,25 @@ __device__ __forceinline__ bf16x8 deq_int4x8(uint32_t w, uint32_t meta) {
   if (__builtin_expect(s9 <= 3.4028234663852886e38f, 1)) return deq_int4x8_fp8(w, s9, z);
   return deq_int4x8_ubyte(w, s, z);
 }
+__device__ __forceinline__ bf16x8 deq_int4x8(uint32_t w, u32x2 meta) {
+  const float s = meta_scale(meta), z = meta_zero(meta);
+  const float s9 = s * 512.0f;
+  if (__builtin_expect(s9 <= 3.4028234663852886e38f, 1)) return deq_int4x8_fp8_ma(w, s9, z);
+  return deq_int4x8_ubyte_ma(w, s, z);
+}
+
+// The RoPE group's 8 codes on the fp8 path (s9 = s * 2^9 finite), with the
+// arithmetic its metadata type asks for.
+template <int F>
+__device__ __forceinline__ bf16x8 deq_rope8_fp8(uint32_t w, float s9, float z) {
+  if constexpr (Fmt<F>::F32R) return deq_int4x8_fp8_ma(w, s9, z);
+  else return deq_int4x8_fp8(w, s9, z);
+}
 
 // The lane's 64 content dims -> 8 slices of 8 bf16 (dims 8t .. 8t+7 of them).
 template <int F>
 __device__ __forceinline__ void deq_content(const Packed<F>& p, bf16x8* kv) {
-  if constexpr (F == 0) {
+  if constexpr (Fmt<F>::CBITS == 4) {
     const float s = meta_scale(p.mc), z = meta_zero(p.mc);
     const float s9 = s * 512.0f;
     if (__builtin_expect(s9 <= 3.4028234663852886e38f, 1)) {

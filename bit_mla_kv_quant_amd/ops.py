@@ -15,7 +15,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmla_lowbit.so")
 
-FORMATS = {"C4R4": 0, "C2R4": 1}
+FORMATS = {"C4R4": 0, "C2R4": 1, "C4R4F": 2}
 
 ERRORS = {0: "MLA_LB_OK", -1: "MLA_LB_EINVAL", -2: "MLA_LB_ESHAPE", -3: "MLA_LB_EFORMAT",
           -4: "MLA_LB_EWORKSPACE", -5: "MLA_LB_EHIP"}

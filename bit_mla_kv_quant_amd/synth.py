@@ -39,7 +39,7 @@ PAGE = 64
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    fmt: str                 # "C4R4" or "C2R4"
+    fmt: str                 # "C4R4", "C2R4" or "C4R4F"
     batch: int
     heads: int
     len_lo: int              # inclusive range of context lengths

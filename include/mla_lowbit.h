@@ -35,15 +35,21 @@
  *                    16+2m..17+2m (m = 0..7)
  *     codes_r  [64 tok][32 B], byte k holds RoPE dims 2k (lo) and 2k+1 (hi)
  *     meta_c   [64 tok][8 groups][scale, zero] bf16
- *     meta_r   [64 tok][scale, zero] bf16
- *   Page bytes: C4R4 20736 (324 per token), C2R4 12544 (196 per token).
+ *     meta_r   [64 tok][scale, zero] bf16; C4R4F: [64 tok][scale, zero]
+ *              fp32 (content regions as C4R4)
+ *   Page bytes: C4R4 20736 (324 per token), C2R4 12544 (196 per token),
+ *   C4R4F 20992 (328 per token).
  *
  * Quantizer [QuantMLA §4.1, App. C.4] (per token, per group of 64 values x,
  * m = 2^bits - 1, all arithmetic IEEE fp32, round-to-nearest-even):
  *     s = bf16(fl32(fl32(max x - min x) / m)),  z = min x (bf16-exact),
  *     q = clamp(rint(fl32(fl32(x - z) / s)), 0, m), or q = 0 when s == 0,
  *     reconstruction x^ = bf16(fl32(q * s + z)).
- * Content groups use bits 4 (C4R4) or 2 (C2R4); the RoPE group uses 4 bits.
+ * Content groups use bits 4 (C4R4, C4R4F) or 2 (C2R4); the RoPE group uses
+ * 4 bits.  C4R4F's RoPE group keeps fp32 metadata instead:
+ *     s = fl32(fl32(max x - min x) / 15),  z = min x,
+ *     q = clamp(rint(fl32(fl32(x - z) / s)), 0, 15), or q = 0 when s == 0,
+ *     reconstruction x^ = bf16(fl32(fl32(q * s) + z))  (product rounded first).
  *
  * BF16 protection buffer [QuantMLA §3.3, App. C.5]: per sequence slot,
  * prot[132][576] bf16, a row = [c (512) | k_R (64)].  Token position i < 4
@@ -62,8 +68,9 @@ extern "C" {
 #endif
 
 /* Cache formats, CxRy = x-bit content cache, y-bit RoPE-key cache
- * [QuantMLA §4.1]. */
-typedef enum { MLA_LB_C4R4 = 0, MLA_LB_C2R4 = 1 } mla_lb_format;
+ * [QuantMLA §4.1].  MLA_LB_C4R4F is C4R4 with the RoPE group's scale and
+ * zero kept in fp32, as the pages store RoPE scales [QuantMLA App. C.4/C.5]. */
+typedef enum { MLA_LB_C4R4 = 0, MLA_LB_C2R4 = 1, MLA_LB_C4R4F = 2 } mla_lb_format;
 
 enum {
   MLA_LB_OK = 0,
@@ -88,7 +95,7 @@ int mla_lb_version(void);
 /* Static message for an error code (host, pure, never NULL). */
 const char* mla_lb_strerror(int code);
 
-/* Bytes of one physical page of format f (20736 / 12544), 0 if f is unknown
+/* Bytes of one physical page of format f (20736 / 12544 / 20992), 0 if f is unknown
  * (host, pure). */
 size_t mla_lb_page_bytes(int f);
 

@@ -42,6 +42,8 @@ def test_pure_host_queries(ops):
     assert ops.mla_lb_version() >= 1
     assert ops.mla_lb_page_bytes("C4R4") == 20736
     assert ops.mla_lb_page_bytes("C2R4") == 12544
+    assert ops.mla_lb_page_bytes("C4R4F") == 20992
+    assert ops.mla_lb_page_bytes(3) == 0
     assert ops.mla_lb_page_bytes(7) == 0
     assert ops.mla_lb_prot_bytes_per_seq() == 152064
     for c in (0, -1, -2, -3, -4, -5, -99):
@@ -83,7 +85,7 @@ def _decode(lib, f=0, B=2, H=16, max_blocks=4, msl=200, scale=0.07, ns=0, ws=Non
 
 def test_decode_validation(ops):
     lib = ops.raw()
-    assert _decode(lib, f=2) == -3
+    assert _decode(lib, f=3) == -3
     for k in ("q_lat", "q_rope", "pages", "prot", "seq_slot", "block_table", "seq_lens", "out", "lse"):
         assert _decode(lib, null=k) == -1, k
     assert _decode(lib, scale=0.0) == -1

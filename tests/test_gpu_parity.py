@@ -41,7 +41,7 @@ def check_decode(d, cache, out, lse, lens, which=None, fmt=None):
 
 
 # --------------------------------------------------------------- writer ---
-@pytest.mark.parametrize("fmt", ["C4R4", "C2R4"])
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "C4R4F"])
 def test_append_pages_and_prot_bit_exact(fmt):
     d = synth.small(fmt=fmt, batch=3, heads=16, lens=(300, 77, 133), seed=3, spare_pages=2)
     say("append", fmt, d.lens.tolist())
@@ -62,7 +62,7 @@ def test_append_pages_and_prot_bit_exact(fmt):
         assert not prot[b, unused].any()
 
 
-@pytest.mark.parametrize("fmt", ["C4R4", "C2R4"])
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "C4R4F"])
 def test_dequant_dump_bit_exact(fmt):
     from bit_mla_kv_quant_amd import ops
     d = synth.small(fmt=fmt, batch=2, heads=16, lens=(256, 100), seed=4, outlier_factor=16.0)
@@ -76,11 +76,12 @@ def test_dequant_dump_bit_exact(fmt):
         np.testing.assert_array_equal(got, want, err_msg=f"page {pid}")
 
 
-def test_dequant_edge_values():
+@pytest.mark.parametrize("fmt", ["C4R4", "C4R4F"])
+def test_dequant_edge_values(fmt):
     """Constant groups, tiny (subnormal-scale) ranges and huge ranges survive
     the GPU writer and reconstruction bit for bit."""
     from bit_mla_kv_quant_amd import ops
-    d = synth.small(fmt="C4R4", batch=1, heads=16, lens=(64,), seed=5)
+    d = synth.small(fmt=fmt, batch=1, heads=16, lens=(64,), seed=5)
     rng = np.random.default_rng(5)
     c = quant.bf16_to_f32(d.c[0]).copy()
     c[0, :] = 1.25                                   # constant groups
@@ -91,15 +92,17 @@ def test_dequant_edge_values():
     d.c[0] = quant.f32_to_bf16(c.astype(np.float32))
     kr = quant.bf16_to_f32(d.kr[0]).copy()
     kr[5, :] = -3.0
+    kr[6, :] = rng.standard_normal(64) * 1e-38       # subnormal RoPE range
+    kr[7, :] = rng.standard_normal(64) * 1e30        # huge RoPE values
     d.kr[0] = quant.f32_to_bf16(kr.astype(np.float32))
-    say("dequant_edge")
+    say("dequant_edge", fmt)
     g = GpuCache(d)
     g.fill()
     torch.cuda.synchronize()
     np.testing.assert_array_equal(g.pages.cpu().numpy()[d.block_table[0, 0]],
                                   oracle_page(d, d.block_table[0, 0], d.lens))
-    got = ops.mla_lb_dequant_dump("C4R4", g.pages, int(d.block_table[0, 0])).cpu().numpy().view(np.uint16)
-    want = quant.dequantize_tokens(quant.quantize_tokens(d.c[0], d.kr[0], "C4R4"))
+    got = ops.mla_lb_dequant_dump(fmt, g.pages, int(d.block_table[0, 0])).cpu().numpy().view(np.uint16)
+    want = quant.dequantize_tokens(quant.quantize_tokens(d.c[0], d.kr[0], fmt))
     np.testing.assert_array_equal(got, want)
 
 
@@ -107,7 +110,7 @@ def test_dequant_edge_values():
 EDGE_LENS = (0, 1, 3, 4, 5, 63, 64, 65, 127, 128, 129, 131, 132, 133, 200, 1000)
 
 
-@pytest.mark.parametrize("fmt", ["C4R4", "C2R4"])
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "C4R4F"])
 @pytest.mark.parametrize("H", [16, 32, 128])
 def test_decode_edge_lengths(fmt, H):
     d = synth.small(fmt=fmt, batch=len(EDGE_LENS), heads=H, lens=EDGE_LENS, seed=H)
@@ -120,7 +123,7 @@ def test_decode_edge_lengths(fmt, H):
         say("  num_splits", ns, "worst rel-L2", f"{w:.2e}")
 
 
-@pytest.mark.parametrize("fmt", ["C4R4", "C2R4"])
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "C4R4F"])
 def test_split_invariance_and_determinism(fmt):
     d = synth.small(fmt=fmt, batch=4, heads=16, lens=(2000, 1500, 640, 4096), seed=9)
     say("split_invariance", fmt)
@@ -183,7 +186,7 @@ def test_score_jumps(H):
         say("  num_splits", ns, "worst rel-L2", f"{w:.2e}")
 
 
-@pytest.mark.parametrize("fmt", ["C4R4", "C2R4"])
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "C4R4F"])
 def test_token_aging(fmt):
     """Append one token per step from L=1 to 300 and decode each step: a
     token's packed bytes never change after insertion, tokens leaving the
@@ -211,12 +214,13 @@ def test_token_aging(fmt):
 
 
 def _slot_regions(fmt, off):
-    nblk = 4 if fmt == "C4R4" else 2
+    nblk = 2 if fmt == "C2R4" else 4
+    mr = 8 if fmt == "C4R4F" else 4                  # RoPE (scale, zero) bytes
     base_r = 64 * 64 * nblk
     out = [slice((b * 64 + off) * 64, (b * 64 + off) * 64 + 64) for b in range(nblk)]
     out.append(slice(base_r + off * 32, base_r + off * 32 + 32))
     out.append(slice(base_r + 2048 + off * 32, base_r + 2048 + off * 32 + 32))
-    out.append(slice(base_r + 4096 + off * 4, base_r + 4096 + off * 4 + 4))
+    out.append(slice(base_r + 4096 + off * mr, base_r + 4096 + off * mr + mr))
     return out
 
 
