@@ -43,7 +43,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PAGE = 64
 PROT_ROWS = 132
 ROW_BYTES = 576 * 2            # one bf16 cache row [c | k_R]
-TOKEN_BYTES = {"C4R4": 324, "C2R4": 196}   # packed codes + bf16 (scale, zero) per token
+TOKEN_BYTES = {"C4R4": 324, "C2R4": 196, "C4R4F": 328}   # packed codes + (scale, zero) per token
 KERNEL_SOURCES = ("bit_mla_kv_quant_amd/csrc/decode.hip", "bit_mla_kv_quant_amd/csrc/decode_h16.hip",
                   "bit_mla_kv_quant_amd/csrc/decode_h128.hip", "bit_mla_kv_quant_amd/csrc/dequant.h",
                   "bit_mla_kv_quant_amd/csrc/common.h")
@@ -187,7 +187,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1, help="synthetic workload id (0-4)")
+    ap.add_argument("--config", type=int, default=1, help="synthetic workload id (0-5)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graphs")
     ap.add_argument("--splits", type=int, default=0,

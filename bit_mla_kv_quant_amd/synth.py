@@ -62,6 +62,8 @@ WORKLOADS = {
                 outlier_factor=16.0, seed=20263),
     4: Workload("pressure_c4r4_b8_h128_l96k_128k", "C4R4", 8, 128, 98304, 131072,
                 append_steps=8, seed=20264),
+    # the V2-Lite shape in the fp32-RoPE-metadata format [QuantMLA App. C.4/C.5]
+    5: Workload("v2lite_c4r4f_b32_h16_l8k", "C4R4F", 32, 16, 8192, 8192, seed=20265),
 }
 
 SOFTMAX_SCALE = 1.0 / math.sqrt(192.0)

@@ -260,6 +260,10 @@ def test_config3_v2_h128():
     _full_config(3, sample_b=[0, 15])
 
 
+def test_config5_v2lite_fp32_rope_metadata():
+    _full_config(5, sample_b=[0, 31])
+
+
 def test_config4_pressure_with_append_steps():
     d, c = _full_config(4, sample_b=[0])
     lens = d.lens.astype(np.int64).copy()
