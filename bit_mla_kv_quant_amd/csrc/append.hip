@@ -17,18 +17,59 @@
 
 namespace mlb {
 
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
-  return v;
+// Cross-lane steps use DPP within each row of 16 lanes and the gfx950 row
+// swaps across rows, so a reduction never waits on the LDS crossbar.
+constexpr int DPP_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <-> 7-i within each 8
+constexpr int DPP_MIRROR = 0x140;       // lane i <-> 15-i within each 16
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __uint_as_float(dpp<CTRL>(__float_as_uint(v)));
 }
-__device__ __forceinline__ uint32_t or_reduce(uint32_t v, int width) {
-  for (int o = 1; o < width; o <<= 1) v |= __shfl_xor(v, o, 64);
+
+// Combine the lane's value with its partners in the other three rows of 16
+// (the value is already uniform within each row).
+template <typename Op>
+__device__ __forceinline__ float across_rows(float x, Op op) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+  x = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+  return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
+struct MinOp {
+  __device__ float operator()(float a, float b) const { return fminf(a, b); }
+};
+struct MaxOp {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, dppf<DPP_XOR1>(v));
+  v = op(v, dppf<DPP_XOR2>(v));
+  v = op(v, dppf<DPP_HALF_MIRROR>(v));
+  v = op(v, dppf<DPP_MIRROR>(v));
+  return across_rows(v, op);
+}
+__device__ __forceinline__ float wave_min(float v) { return wave_reduce(v, MinOp{}); }
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, MaxOp{}); }
+
+// OR over aligned runs of 8 or 16 lanes (every lane of the run gets it).
+template <int WIDTH>
+__device__ __forceinline__ uint32_t or_reduce(uint32_t v) {
+  v |= dpp<DPP_XOR1>(v);
+  v |= dpp<DPP_XOR2>(v);
+  v |= dpp<DPP_HALF_MIRROR>(v);
+  if constexpr (WIDTH == 16) v |= dpp<DPP_MIRROR>(v);
   return v;
 }
 
@@ -69,7 +110,8 @@ template <int F>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   using FM = Fmt<F>;
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform token index: its arguments come in through scalar loads
+  const int t = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= a.T) return;
   const int64_t slot = a.slot_mapping[t];
   const int sq = a.seq_slot[t];
@@ -98,14 +140,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int dib = d % FM::DPB;                   // dim within block
     if (FM::CBITS == 4) {
       // byte k = dims 2k (lo), 2k+1 (hi): dword = dims 8w..8w+7, nibble d%8
-      const uint32_t w = or_reduce(q << (4 * (lane & 7)), 8);
+      const uint32_t w = or_reduce<8>(q << (4 * (lane & 7)));
       if ((lane & 7) == 0)
         *(uint32_t*)(pg + (blk * PAGE + off) * 64 + (dib / 8) * 4) = w;
     } else {
       // dword = dims 16w..16w+15: dim 16w+2m at bits 2m, dim 16w+2m+1 at
       // bits 16+2m
       const int e = lane & 15;
-      const uint32_t w = or_reduce(q << (16 * (e & 1) + 2 * (e >> 1)), 16);
+      const uint32_t w = or_reduce<16>(q << (16 * (e & 1) + 2 * (e >> 1)));
       if ((lane & 15) == 0)
         *(uint32_t*)(pg + (blk * PAGE + off) * 64 + (dib / 16) * 4) = w;
     }
@@ -115,14 +157,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   if constexpr (FM::F32R) {
     float s32, z32;
     const uint32_t q = quantize_lane_f32(bf16_bits_to_f32(xr), 4, s32, z32);
-    const uint32_t w = or_reduce(q << (4 * (lane & 7)), 8);
+    const uint32_t w = or_reduce<8>(q << (4 * (lane & 7)));
     if ((lane & 7) == 0) *(uint32_t*)(pg + FM::OFF_R + off * 32 + (lane / 8) * 4) = w;
     if (lane == 0)
       *(u32x2*)(pg + FM::OFF_MR + off * 8) = u32x2{__float_as_uint(s32), __float_as_uint(z32)};
   } else {
     uint32_t sb, zb;
     const uint32_t q = quantize_lane(bf16_bits_to_f32(xr), 4, sb, zb);
-    const uint32_t w = or_reduce(q << (4 * (lane & 7)), 8);
+    const uint32_t w = or_reduce<8>(q << (4 * (lane & 7)));
     if ((lane & 7) == 0) *(uint32_t*)(pg + FM::OFF_R + off * 32 + (lane / 8) * 4) = w;
     if (lane == 0) *(uint32_t*)(pg + FM::OFF_MR + off * 4) = sb | (zb << 16);
   }

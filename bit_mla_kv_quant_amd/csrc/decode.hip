@@ -19,24 +19,28 @@ namespace mlb {
 // merges head 16*blockIdx.y + hh, dims 64*blockIdx.x + 4c .. +3 over the
 // sequence's splits: m* = max m_j, weights e^(m_j - m*), out = sum w_j o_j /
 // sum w_j l_j, lse = m* + ln sum w_j f_j  [QuantMLA App. C.5].
+// Every split of the grid has written its (m, l, f): a split past the end of
+// its sequence writes m = -inf and no O, so the merge needs no sequence
+// length and starts with all its loads in flight.  A split's O is read only
+// when its m is finite; a sequence with no finite m gets out 0, lse -inf.
+__device__ __forceinline__ void combine_term(const f32x4& ml, const f32x4& ov, float M, f32x4& accv,
+                                             float& ssum, float& fsum) {
+  if (ml[0] != -INFINITY) {
+    const float wgt = __builtin_amdgcn_exp2f(ml[0] - M);
+    ssum += wgt * ml[1];
+    fsum += wgt * ml[2];
+    accv += wgt * ov;
+  }
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int b = blockIdx.z, H = a.H;
   const int hh = threadIdx.x >> 4, c = threadIdx.x & 15;
   const int h = blockIdx.y * 16 + hh;
   const int d0 = 64 * blockIdx.x + 4 * c;
-  int L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
-  const int sq = a.seq_slot[b];
-  if (sq < 0 || sq >= a.num_seq_slots) L = 0;
-  const int npages = (L + PAGE - 1) / PAGE;
-  const int ns = (npages + a.pps - 1) / a.pps;
+  const int ns = a.nsplit;
   float* o = a.out + ((int64_t)b * H + h) * DC + d0;
-  if (ns == 0) {
-    *(f32x4*)o = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (blockIdx.x == 0 && c == 0) a.lse[(int64_t)b * H + h] = -INFINITY;
-    return;
-  }
-  const int64_t base = (int64_t)b * a.nsplit * H + h;     // split jj at base + jj*H
+  const int64_t base = (int64_t)b * ns * H + h;          // split jj at base + jj*H
   f32x4 accv = {0.f, 0.f, 0.f, 0.f};
   float ssum = 0.f, fsum = 0.f, M = -INFINITY;
   if (ns <= 8) {
@@ -54,14 +58,8 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     for (int u = 0; u < 8; ++u)
       if (u < ns) M = fmaxf(M, ml[u][0]);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (u < ns) {
-        const float wgt = ml[u][0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[u][0] - M);
-        ssum += wgt * ml[u][1];
-        fsum += wgt * ml[u][2];
-        accv += wgt * ov[u];
-      }
-    }
+    for (int u = 0; u < 8; ++u)
+      if (u < ns) combine_term(ml[u], ov[u], M, accv, ssum, fsum);
   } else {
     for (int jj = 0; jj < ns; ++jj) M = fmaxf(M, a.ws_ml[(base + (int64_t)jj * H) * 4]);
     int jj = 0;
@@ -74,21 +72,18 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
         ov[u] = *(const f32x4*)(a.ws_o + e * DC + d0);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float wgt = ml[u][0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[u][0] - M);
-        ssum += wgt * ml[u][1];
-        fsum += wgt * ml[u][2];
-        accv += wgt * ov[u];
-      }
+      for (int u = 0; u < 4; ++u) combine_term(ml[u], ov[u], M, accv, ssum, fsum);
     }
     for (; jj < ns; ++jj) {
       const int64_t e = base + (int64_t)jj * H;
-      const f32x4 ml = *(const f32x4*)(a.ws_ml + e * 4);
-      const float wgt = ml[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[0] - M);
-      ssum += wgt * ml[1];
-      fsum += wgt * ml[2];
-      accv += wgt * *(const f32x4*)(a.ws_o + e * DC + d0);
+      combine_term(*(const f32x4*)(a.ws_ml + e * 4), *(const f32x4*)(a.ws_o + e * DC + d0), M,
+                   accv, ssum, fsum);
     }
+  }
+  if (M == -INFINITY) {                              // empty sequence
+    *(f32x4*)o = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (blockIdx.x == 0 && c == 0) a.lse[(int64_t)b * H + h] = -INFINITY;
+    return;
   }
   *(f32x4*)o = accv * (1.0f / ssum);
   if (blockIdx.x == 0 && c == 0)

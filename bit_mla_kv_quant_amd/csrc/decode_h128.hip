@@ -89,6 +89,9 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
       for (int idx = threadIdx.x; idx < HB * DC / 4; idx += 256)
         *(f32x4*)(o + 4 * idx) = f32x4{0.f, 0.f, 0.f, 0.f};
       if (threadIdx.x < HB) a.lse[(int64_t)b * H + HB * hb + threadIdx.x] = -INFINITY;
+    } else if (!single && threadIdx.x < HB) {      // no tokens: m = -inf for the merge
+      const int64_t base = ((int64_t)b * a.nsplit + j) * H + HB * hb + threadIdx.x;
+      *(f32x4*)(a.ws_ml + base * 4) = f32x4{-INFINITY, 0.f, 0.f, 0.f};
     }
     return;
   }

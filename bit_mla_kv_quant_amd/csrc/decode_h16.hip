@@ -95,6 +95,9 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
       for (int idx = threadIdx.x; idx < 16 * DC / 4; idx += 512)
         *(f32x4*)(o + 4 * idx) = f32x4{0.f, 0.f, 0.f, 0.f};
       if (threadIdx.x < 16) a.lse[(int64_t)b * H + 16 * hg + threadIdx.x] = -INFINITY;
+    } else if (!single && threadIdx.x < 16) {      // no tokens: m = -inf for the merge
+      const int64_t base = ((int64_t)b * a.nsplit + j) * H + 16 * hg + threadIdx.x;
+      *(f32x4*)(a.ws_ml + base * 4) = f32x4{-INFINITY, 0.f, 0.f, 0.f};
     }
     return;
   }
