@@ -1,11 +1,13 @@
 """Benchmark of the low-bit MLA decode hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config N] [--no-cpu] [--no-graph]
+    python bench.py [--steps K] [--warmup W] [--config N] [--step fused|separate] [--no-cpu] [--no-graph]
 
-One step = one decode step of a whole batch through the C ABI:
-kv_quant_append of each sequence's current token (quantize, pack, slot-mapped
-insert, BF16 window refresh), then mla_decode_lowbit over every cached token
-(paged low-bit + BF16 protected rows, one global softmax, split-KV merge).
+One step = one decode step of a whole batch through the C ABI: the writer
+for each sequence's current token (quantize, pack, slot-mapped insert, BF16
+window refresh), then decode over every cached token (paged low-bit + BF16
+protected rows, one global softmax, split-KV merge).  By default both run in
+one launch (mla_decode_lowbit_append); --step separate times kv_quant_append
+followed by mla_decode_lowbit.
 The headline workload is the DeepSeek-V2-Lite-shaped C4R4 cache: batch 32,
 16 heads, 8192 tokens per sequence, 64-token pages with a shuffled block table.
 
@@ -192,6 +194,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graphs")
     ap.add_argument("--splits", type=int, default=0,
                     help="splits per max-length sequence (0: the library's automatic plan)")
+    ap.add_argument("--step", choices=("fused", "separate"), default="fused",
+                    help="fused: mla_decode_lowbit_append (writer inside the decode launch); "
+                         "separate: kv_quant_append then mla_decode_lowbit")
     ap.add_argument("--min-rotation-gib", type=float, default=1.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (HBM counter calibration)")
@@ -245,9 +250,20 @@ def main():
                               workspace=r["ws"] if ws_bytes else None, out=r["out"],
                               lse=r["lse"], stream=stream)
 
+    def do_fused(r):
+        s = r["step"]
+        ops.mla_decode_lowbit_append(fmt, s["latent"], s["k_rope"], r["q_lat"], r["q_rope"],
+                                     r["pages"], r["prot"], r["seq_slot"], r["block_table"],
+                                     r["seq_lens"], max_len, d.scale, args.splits,
+                                     workspace=r["ws"] if ws_bytes else None, out=r["out"],
+                                     lse=r["lse"], stream=stream)
+
     def do_step(r):
-        do_append(r)
-        do_decode(r)
+        if args.step == "fused":
+            do_fused(r)
+        else:
+            do_append(r)
+            do_decode(r)
 
     use_graph = not args.no_graph
     steps_fn, dec_fn = [], []
@@ -348,7 +364,9 @@ def main():
                    "context": [min(lens), max(lens)], "page_tokens": PAGE,
                    "d_c": 512, "d_r": 64, "sink": 4, "recent": 128, "replicas": R,
                    "hip_graph": use_graph, "parallelism": "split-kv on 1 GPU",
-                   "step": "kv_quant_append(B tokens) + mla_decode_lowbit"},
+                   "step": ("mla_decode_lowbit_append (writer of the B new tokens fused "
+                            "into the decode launch)" if args.step == "fused" else
+                            "kv_quant_append(B tokens) + mla_decode_lowbit")},
         "roofline": roof,
         "decode_kv_tokens_per_s": round(kv_tokens / (dec_ms * 1e-3), 1),
         "append_ms": round(app_ms, 5),

@@ -99,13 +99,19 @@ int mla_decode_lowbit_workspace(int f, int32_t B, int32_t H, int32_t max_seq_len
   return MLA_LB_OK;
 }
 
-int mla_decode_lowbit(int f, const uint16_t* q_lat, const uint16_t* q_rope,
-                      const uint8_t* pages, int64_t num_pages, const uint16_t* prot,
-                      int32_t num_seq_slots, const int32_t* seq_slot,
-                      const int32_t* block_table, int32_t max_blocks,
-                      const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t H,
-                      float softmax_scale, int32_t num_splits, void* workspace,
-                      size_t workspace_bytes, float* out, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and dispatch shared by the decode entry points.  new_c / new_r
+// non-null selects the fused writer (pages / prot are then written).
+int decode_entry(int f, const uint16_t* q_lat, const uint16_t* q_rope, const uint8_t* pages,
+                 int64_t num_pages, const uint16_t* prot, int32_t num_seq_slots,
+                 const int32_t* seq_slot, const int32_t* block_table, int32_t max_blocks,
+                 const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t H,
+                 float softmax_scale, int32_t num_splits, void* workspace,
+                 size_t workspace_bytes, float* out, float* lse, void* stream,
+                 const uint16_t* new_c, const uint16_t* new_r) {
   if (mlb::page_bytes_of(f) == 0) return MLA_LB_EFORMAT;
   if (!q_lat || !q_rope || !pages || !prot || !seq_slot || !block_table || !seq_lens || !out ||
       !lse)
@@ -143,7 +149,41 @@ int mla_decode_lowbit(int f, const uint16_t* q_lat, const uint16_t* q_rope,
   a.ws_ml = plan.nsplit > 1 ? ws + n_o : nullptr;
   a.out = out;
   a.lse = lse;
+  a.new_c = new_c;
+  a.new_r = new_r;
+  a.wpages = const_cast<uint8_t*>(pages);
+  a.wprot = const_cast<uint16_t*>(prot);
   return mlb::launch_decode(f, a, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_lowbit(int f, const uint16_t* q_lat, const uint16_t* q_rope,
+                      const uint8_t* pages, int64_t num_pages, const uint16_t* prot,
+                      int32_t num_seq_slots, const int32_t* seq_slot,
+                      const int32_t* block_table, int32_t max_blocks,
+                      const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t H,
+                      float softmax_scale, int32_t num_splits, void* workspace,
+                      size_t workspace_bytes, float* out, float* lse, void* stream) {
+  return decode_entry(f, q_lat, q_rope, pages, num_pages, prot, num_seq_slots, seq_slot,
+                      block_table, max_blocks, seq_lens, max_seq_len, B, H, softmax_scale,
+                      num_splits, workspace, workspace_bytes, out, lse, stream, nullptr, nullptr);
+}
+
+int mla_decode_lowbit_append(int f, const uint16_t* latent, const uint16_t* k_rope,
+                             const uint16_t* q_lat, const uint16_t* q_rope, uint8_t* pages,
+                             int64_t num_pages, uint16_t* prot, int32_t num_seq_slots,
+                             const int32_t* seq_slot, const int32_t* block_table,
+                             int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
+                             int32_t B, int32_t H, float softmax_scale, int32_t num_splits,
+                             void* workspace, size_t workspace_bytes, float* out, float* lse,
+                             void* stream) {
+  if (!latent || !k_rope) return mlb::page_bytes_of(f) == 0 ? MLA_LB_EFORMAT : MLA_LB_EINVAL;
+  return decode_entry(f, q_lat, q_rope, pages, num_pages, prot, num_seq_slots, seq_slot,
+                      block_table, max_blocks, seq_lens, max_seq_len, B, H, softmax_scale,
+                      num_splits, workspace, workspace_bytes, out, lse, stream, latent, k_rope);
 }
 
 int mla_lb_dequant_dump(int f, const uint8_t* pages, int64_t num_pages, int64_t page_id,

@@ -40,6 +40,7 @@
 #include "common.h"
 #include "dequant.h"
 #include "internal.h"
+#include "quantize.h"
 
 namespace mlb {
 
@@ -96,6 +97,10 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
     return;
   }
   const int np = p1 - p0;
+  // fused writer: the first split of head block 0 stores the newest token
+  const bool fused = a.new_c != nullptr;
+  if (fused && j == 0 && hb == 0)
+    fused_append<F>(a, b, L, sq, __builtin_amdgcn_readfirstlane(wave), 4, lane);
 
   const __attribute__((address_space(4))) int32_t* bt_row =
       (const __attribute__((address_space(4))) int32_t*)(a.block_table +
@@ -156,9 +161,14 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
       const int i = (p0 + k) * PAGE + tt;
       const bool valid = phys >= 0 && i < L;
       const bool prot = valid && is_protected(i, L);
+      // bf16 row of a protected token: its protection-buffer row, or for the
+      // token the fused writer stores in this call, the new row itself
+      const bool fresh = fused && i == L - 1;
       const uint16_t* prow = prot_seq + (int64_t)(prot ? prot_row(i) : 0) * DROW;
+      const uint16_t* pc = fresh ? a.new_c + (int64_t)b * DC : prow;
+      const uint16_t* pr = fresh ? a.new_r + (int64_t)b * DR : prow + DC;
       auto fix = [&](const bf16x8 v, const int off) -> bf16x8 {
-        if (prot) return *(const bf16x8*)(prow + off);
+        if (prot) return off < DC ? *(const bf16x8*)(pc + off) : *(const bf16x8*)(pr + (off - DC));
         return valid ? v : bitcast<bf16x8>(u32x4{0u, 0u, 0u, 0u});
       };
 #pragma unroll

@@ -39,6 +39,7 @@
 #include "common.h"
 #include "dequant.h"
 #include "internal.h"
+#include "quantize.h"
 
 namespace mlb {
 
@@ -102,6 +103,9 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
     return;
   }
   const int nquart = 4 * (p1 - p0);                // quarter pages of the split
+  // fused writer: the first split of head group 0 stores the newest token
+  const bool fused = a.new_c != nullptr;
+  if (fused && j == 0 && hg == 0) fused_append<F>(a, b, L, sq, wave, NW, lane);
 
   const __attribute__((address_space(4))) int32_t* bt_row =
       (const __attribute__((address_space(4))) int32_t*)(a.block_table +
@@ -193,12 +197,20 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
       const int i = i0 + n16;
       const bool valid = phys >= 0 && i < L;
       const bool prot = valid && is_protected(i, L);
+      // bf16 row of a protected token: its protection-buffer row, or for the
+      // token the fused writer stores in this call, the new row itself
+      const bool fresh = fused && i == L - 1;
       const uint16_t* prow = prot_seq + (int64_t)(prot ? prot_row(i) : 0) * DROW;
+      const uint16_t* pc = fresh ? a.new_c + (int64_t)b * DC : prow;
+      const uint16_t* pr = fresh ? a.new_r + (int64_t)b * DR : prow + DC;
+      auto prot_at = [&](const int off) -> bf16x8 {  // dims off .. off+7 of the row
+        return off < DC ? *(const bf16x8*)(pc + off) : *(const bf16x8*)(pr + (off - DC));
+      };
       auto slice_off = [&](const int s) {            // row offset of slice s
         return s < 16 ? 128 * g + 8 * s : DC + 16 * g + 8 * (s - 16);
       };
       auto prot_slice = [&](const int s) -> bf16x8 {
-        return prot ? *(const bf16x8*)(prow + slice_off(s)) : bitcast<bf16x8>(u32x4{0u, 0u, 0u, 0u});
+        return prot ? prot_at(slice_off(s)) : bitcast<bf16x8>(u32x4{0u, 0u, 0u, 0u});
       };
       if (__all(prot)) {
         // a quarter of the recent window: nothing to reconstruct, so slice s
@@ -207,7 +219,7 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
         auto off_p = [&](const int s) { return (s < 16 ? 32 * s : DC + 32 * (s - 16)) + 8 * g; };
         bf16x8 pr[18];
 #pragma unroll
-        for (int s = 0; s < 18; ++s) pr[s] = *(const bf16x8*)(prow + off_p(s));
+        for (int s = 0; s < 18; ++s) pr[s] = prot_at(off_p(s));
 #pragma unroll
         for (int s = 0; s < 18; ++s) {
           const bf16x8 qs = *(const bf16x8*)(qrow + off_p(s));

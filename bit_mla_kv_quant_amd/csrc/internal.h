@@ -41,6 +41,13 @@ struct DecodeArgs {
   float* ws_ml;          // [B][nsplit][H][4]   (max in log2 units, bf16-weight sum, fp32 sum, 0)
   float* out;            // [B][H][512]
   float* lse;            // [B][H]
+  // fused writer (null new_c: decode only): token seq_lens[b]-1 of sequence
+  // b is new_c[b] / new_r[b]; the kernel stores its packed copy and bf16
+  // protection row, and reads that token from new_c / new_r
+  const uint16_t* new_c;  // [B][512] bf16
+  const uint16_t* new_r;  // [B][64]  bf16
+  uint8_t* wpages;        // == pages
+  uint16_t* wprot;        // == prot
 };
 
 // Split plan: how a max_seq_len sequence is cut into splits.

@@ -190,6 +190,36 @@ int mla_decode_lowbit(int f, const uint16_t* q_lat, const uint16_t* q_rope,
                       float* lse, void* stream);
 
 /*
+ * mla_decode_lowbit_append -- one decode step with the fused cache writer in
+ * the same launch [QuantMLA App. C.5]: the result equals
+ *   kv_quant_append(f, latent, k_rope, slot_mapping, seq_slot, pos, new_len,
+ *                   B, pages, num_pages, prot, num_seq_slots)
+ * with, for each sequence b of length L = seq_lens[b] >= 1,
+ *   pos = L - 1, new_len = L,
+ *   slot_mapping = block_table[b][(L-1)/64] * 64 + (L-1) % 64,
+ * followed by mla_decode_lowbit(...) with the same remaining arguments --
+ * the same page bytes, protection rows, out and lse.  The token at L - 1 is
+ * the one being decoded: its packed copy and bf16 protection row are stored
+ * for later calls, and this call's attention reads its bf16 row from
+ * latent / k_rope directly.
+ *
+ *   latent [B][512], k_rope [B][64] bf16: the newest token of each sequence
+ *   pages, prot: written (token slots and protection rows as above)
+ *   other arguments, workspace size and errors: as mla_decode_lowbit.
+ * Sequences with L = 0 append nothing; a block-table entry outside
+ * [0, num_pages) for block (L-1)/64 stores nothing (that token then reads as
+ * an unusable slot, as in mla_decode_lowbit).
+ */
+int mla_decode_lowbit_append(int f, const uint16_t* latent, const uint16_t* k_rope,
+                             const uint16_t* q_lat, const uint16_t* q_rope, uint8_t* pages,
+                             int64_t num_pages, uint16_t* prot, int32_t num_seq_slots,
+                             const int32_t* seq_slot, const int32_t* block_table,
+                             int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
+                             int32_t B, int32_t H, float softmax_scale, int32_t num_splits,
+                             void* workspace, size_t workspace_bytes, float* out, float* lse,
+                             void* stream);
+
+/*
  * mla_lb_dequant_dump -- write the bf16 rows the decode kernel reconstructs
  * for every slot of one page, [64][576] = [c^ | k^_R], using the same device
  * code as mla_decode_lowbit.  For checking the reconstruction bit for bit.

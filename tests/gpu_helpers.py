@@ -89,6 +89,33 @@ class GpuCache:
         torch.cuda.synchronize()
         return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
+    def fused_step(self, lens, num_splits=0, max_seq_len=None):
+        """mla_decode_lowbit_append: store token lens[b]-1 of each sequence
+        (lens[b] > 0) and decode over lens[b] tokens, in one call."""
+        d = self.d
+        lens = np.asarray(lens, dtype=np.int64)
+        msl = int(lens.max()) if max_seq_len is None else max_seq_len
+        # an empty sequence appends nothing: its row is never read
+        lat = np.stack([d.c[b][L - 1] if L > 0 else np.zeros(512, np.uint16)
+                        for b, L in enumerate(lens)])
+        kr = np.stack([d.kr[b][L - 1] if L > 0 else np.zeros(64, np.uint16)
+                       for b, L in enumerate(lens)])
+        out, lse = self.ops.mla_decode_lowbit_append(
+            self.fmt, t_bf16(lat), t_bf16(kr), t_bf16(d.q_lat), t_bf16(d.q_rope), self.pages,
+            self.prot, self.seq_slot, self.block_table, t_i32(lens), msl, d.scale,
+            num_splits=num_splits)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+    def clone(self):
+        """A second cache holding the same bytes (same workload)."""
+        other = GpuCache.__new__(GpuCache)
+        other.__dict__.update(self.__dict__)
+        other.pages = self.pages.clone()
+        other.prot = self.prot.clone()
+        other.lens = self.lens.copy()
+        return other
+
 
 def oracle_decode(d, b, L, fmt=None):
     return attention.decode_sequence(d.c[b][:L], d.kr[b][:L], d.q_lat[b], d.q_rope[b],

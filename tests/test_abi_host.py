@@ -106,6 +106,26 @@ def test_decode_validation(ops):
     assert _decode(lib, ns=2, ws=FAKE, ws_bytes=need - 1) == -4
 
 
+def test_fused_step_validation(ops):
+    lib = ops.raw()
+
+    def call(f=0, latent=FAKE, k_rope=FAKE, H=16, scale=0.07, ns=0, ws=None, ws_bytes=0,
+             q_lat=FAKE):
+        return lib.mla_decode_lowbit_append(f, latent, k_rope, q_lat, FAKE, FAKE, 8, FAKE, 2,
+                                            FAKE, FAKE, 4, FAKE, 200, 2, H, scale, ns, ws,
+                                            ws_bytes, FAKE, FAKE, None)
+    assert call(f=3) == -3
+    assert call(f=3, latent=None) == -3
+    assert call(latent=None) == -1
+    assert call(k_rope=None) == -1
+    assert call(q_lat=None) == -1
+    assert call(scale=-1.0) == -1
+    assert call(H=24) == -2
+    need = ops.mla_decode_lowbit_workspace("C4R4", 2, 16, 200, 2)
+    assert call(ns=2) == -4
+    assert call(ns=2, ws=FAKE, ws_bytes=need - 1) == -4
+
+
 def test_dequant_dump_validation(ops):
     lib = ops.raw()
     assert lib.mla_lb_dequant_dump(3, FAKE, 4, 0, FAKE, None) == -3

@@ -213,6 +213,56 @@ def test_token_aging(fmt):
             prev = (pages, L)
 
 
+# ---------------------------------------------------- fused writer + decode ---
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "C4R4F"])
+@pytest.mark.parametrize("H", [16, 32, 128])
+def test_fused_step_equals_append_then_decode(fmt, H):
+    """mla_decode_lowbit_append writes the same page bytes and protection
+    rows as kv_quant_append of each sequence's newest token, and returns the
+    same out / lse bit for bit as mla_decode_lowbit after it; both match the
+    oracle.  Lengths cover the first token, sink edges, page edges, the
+    recent-window edge, several splits and an empty sequence."""
+    lens = np.array([1, 4, 5, 64, 65, 132, 133, 300, 1000, 0])
+    d = synth.small(fmt=fmt, batch=len(lens), heads=H, lens=lens, seed=41)
+    say("fused_step", fmt, H, lens.tolist())
+    base = GpuCache(d)
+    # every sequence holds its first L-1 tokens
+    base.append(list(range(d.B)), [np.arange(max(L - 1, 0)) for L in lens],
+                [max(L - 1, 0) for L in lens])
+    torch.cuda.synchronize()
+    for ns in (0, 1, 3):
+        sep, fus = base.clone(), base.clone()
+        sep.append([b for b in range(d.B) if lens[b] > 0],
+                   [np.array([L - 1]) for L in lens if L > 0], [L for L in lens if L > 0])
+        o1, l1 = sep.decode(lens=lens, num_splits=ns)
+        o2, l2 = fus.fused_step(lens, num_splits=ns)
+        np.testing.assert_array_equal(fus.pages.cpu().numpy(), sep.pages.cpu().numpy())
+        np.testing.assert_array_equal(fus.prot.cpu().numpy(), sep.prot.cpu().numpy())
+        np.testing.assert_array_equal(o2, o1)
+        np.testing.assert_array_equal(l2, l1)
+        w = check_decode(d, fus, o2, l2, lens)
+        say("  num_splits", ns, "worst rel-L2", f"{w:.2e}")
+    pages = fus.pages.cpu().numpy()
+    for pid in range(d.num_pages):
+        np.testing.assert_array_equal(pages[pid], oracle_page(d, pid, lens), err_msg=f"page {pid}")
+
+
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4"])
+def test_fused_token_aging(fmt):
+    """One fused step per token from L=1 to 260: every step matches the
+    oracle, and the pages end byte-identical to the oracle's."""
+    steps = 260
+    d = synth.small(fmt=fmt, batch=2, heads=16, lens=(0, 0), seed=23, extra_tokens=steps)
+    say("fused_token_aging", fmt)
+    c = GpuCache(d)
+    for L in range(1, steps + 1):
+        out, lse = c.fused_step([L, L])
+        check_decode(d, c, out, lse, [L, L])
+    pages = c.pages.cpu().numpy()
+    for pid in range(d.num_pages):
+        np.testing.assert_array_equal(pages[pid], oracle_page(d, pid, [steps, steps]))
+
+
 def _slot_regions(fmt, off):
     nblk = 2 if fmt == "C2R4" else 4
     mr = 8 if fmt == "C4R4F" else 4                  # RoPE (scale, zero) bytes
@@ -268,9 +318,16 @@ def test_config4_pressure_with_append_steps():
     d, c = _full_config(4, sample_b=[0])
     lens = d.lens.astype(np.int64).copy()
     for step in range(d.wl.append_steps):
-        c.append(list(range(d.B)), [np.array([L]) for L in lens], list(lens + 1))
         lens += 1
-        out, lse = c.decode(lens=lens)
-        if step in (0, d.wl.append_steps - 1):
+        if step % 2 == 0:                          # writer, then decode
+            c.append(list(range(d.B)), [np.array([L - 1]) for L in lens], list(lens))
+            out, lse = c.decode(lens=lens)
+        else:                                      # the fused step
+            out, lse = c.fused_step(lens)
+        if step in (0, 1, d.wl.append_steps - 1):
             w = check_decode(d, c, out, lse, lens, which=[0, d.B - 1])
             say("config 4 step", step, "worst rel-L2", f"{w:.2e}")
+    pages = c.pages.cpu().numpy()
+    for b in (0, d.B - 1):
+        for pid in np.unique(d.block_table[b, (lens[b] - d.wl.append_steps) // 64:(lens[b] - 1) // 64 + 1]):
+            np.testing.assert_array_equal(pages[pid], oracle_page(d, pid, lens))
