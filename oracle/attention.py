@@ -27,6 +27,14 @@ What is computed, and where it is stated:
 
 The current decode token is part of the sequence: L counts it (append first,
 then attend over [0, L)).
+
+Several queries per sequence (decode_multi): the last nq tokens of a length-L
+sequence each ask a query, the compute-friendly side of MLA attention
+[MLA blog §7], and each sees only its causal prefix [MLA blog §8]: query j
+(position L - nq + j) attends to [0, L - nq + 1 + j).  The rows every query
+reads are those of the cache at length L -- the protected set P_L -- since
+the cache holds no other state once the nq tokens are written.  (Reading
+taken where the pages are silent; with nq = 1 it is decode_sequence.)
 """
 
 import numpy as np
@@ -128,3 +136,25 @@ def decode_sequence(c_bits, kr_bits, q_lat_bits, q_rope_bits, fmt, scale):
     ql = quant.bf16_to_f32(q_lat_bits).astype(np.float64)
     qr = quant.bf16_to_f32(q_rope_bits).astype(np.float64)
     return attend(ql, qr, rows, scale)
+
+
+def decode_multi(c_bits, kr_bits, q_lat_bits, q_rope_bits, fmt, scale):
+    """Attention of the last nq tokens of one sequence, each over its causal
+    prefix, on the rows of the length-L cache.
+
+    c_bits [L,512], kr_bits [L,64]; q_lat_bits [nq,H,512], q_rope_bits
+    [nq,H,64] (bf16 bits).  returns (out [nq,H,512], lse [nq,H]) float64; a
+    query whose prefix is empty gets 0 and -inf.
+    """
+    rows = effective_rows(c_bits, kr_bits, fmt)
+    L = rows.shape[0]
+    ql = quant.bf16_to_f32(q_lat_bits).astype(np.float64)
+    qr = quant.bf16_to_f32(q_rope_bits).astype(np.float64)
+    nq, H = ql.shape[0], ql.shape[1]
+    out = np.zeros((nq, H, quant.D_C))
+    lse = np.full((nq, H), -np.inf)
+    for j in range(nq):
+        n = L - nq + 1 + j                            # causal prefix of query j
+        if n > 0:
+            out[j], lse[j] = attend(ql[j], qr[j], rows[:n], scale)
+    return out, lse

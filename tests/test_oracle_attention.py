@@ -180,3 +180,60 @@ def test_absorbed_score_and_aggregation_identity():
 
 def test_cache_schema_576():
     assert quant.D_ROW == 576 and quant.D_C == 512 and quant.D_R == 64
+
+
+# ------------------------------------------------- several queries per sequence ---
+def _mq_inputs(L, nq, H, seed, fmt="C4R4"):
+    d = synth.small(fmt=fmt, batch=1, heads=nq * H, lens=(L,), seed=seed)
+    ql = d.q_lat[0].reshape(nq, H, 512)
+    qr = d.q_rope[0].reshape(nq, H, 64)
+    return d.c[0], d.kr[0], ql, qr, d.scale
+
+
+@pytest.mark.parametrize("L,nq", [(1, 1), (7, 3), (40, 8), (132, 5), (133, 9), (300, 16), (5, 8)])
+def test_decode_multi_equals_masked_library_attention(L, nq):
+    """Each query row equals torch SDPA over the cache rows of length L with
+    a boolean mask that admits tokens i <= L - nq + j (library routine; the
+    rows come from effective_rows, pinned above).  Queries whose prefix is
+    empty give 0 / -inf."""
+    H = 2
+    c, kr, ql, qr, scale = _mq_inputs(L, nq, H, seed=L + nq)
+    out, lse = attention.decode_multi(c, kr, ql, qr, "C4R4", scale)
+    rows = attention.effective_rows(c, kr, "C4R4")
+    qf = quant.bf16_to_f32(np.concatenate([ql, qr], axis=2)).astype(np.float64)   # [nq,H,576]
+    for j in range(nq):
+        n = L - nq + 1 + j
+        if n <= 0:
+            assert np.all(out[j] == 0) and np.all(np.isneginf(lse[j]))
+            continue
+        mask = torch.from_numpy(np.arange(L)[None, :] < n).expand(H, L)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(qf[j])[None], torch.from_numpy(rows)[None],
+            torch.from_numpy(rows[:, :512])[None], attn_mask=mask[None], scale=scale)[0].numpy()
+        np.testing.assert_allclose(out[j], ref, rtol=1e-10, atol=1e-12)
+        # the lse is ln of the masked exponential sum (scipy logsumexp)
+        from scipy.special import logsumexp
+        S = scale * (qf[j] @ rows[:n].T)
+        np.testing.assert_allclose(lse[j], logsumexp(S, axis=1), rtol=1e-12, atol=1e-12)
+
+
+def test_decode_multi_last_query_is_single_decode_and_rows_follow_final_length():
+    """The last query sees every token, so it equals decode_sequence; an
+    earlier query reads a token that left the recent window between its
+    position and L through the packed copy (the length-L protected set)."""
+    L, nq, H = 200, 80, 1
+    c, kr, ql, qr, scale = _mq_inputs(L, nq, H, seed=3)
+    out, lse = attention.decode_multi(c, kr, ql, qr, "C4R4", scale)
+    o1, l1 = attention.decode_sequence(c, kr, ql[-1], qr[-1], "C4R4", scale)
+    np.testing.assert_array_equal(out[-1], o1)
+    np.testing.assert_array_equal(lse[-1], l1)
+    # query 0 (position 120) over [0, 121): token 60 is in that prefix's own
+    # recent window but not in P_200, so the packed reconstruction is used
+    rows = attention.effective_rows(c, kr, "C4R4")
+    orig = quant.bf16_to_f32(np.concatenate([c, kr], 1)).astype(np.float64)
+    assert np.any(rows[60] != orig[60])
+    o0, _ = attention.attend(quant.bf16_to_f32(ql[0]).astype(np.float64),
+                             quant.bf16_to_f32(qr[0]).astype(np.float64), rows[:121], scale)
+    np.testing.assert_array_equal(out[0], o0)
+    o_other, _ = attention.decode_sequence(c[:121], kr[:121], ql[0], qr[0], "C4R4", scale)
+    assert np.max(np.abs(o_other - out[0])) > 0
