@@ -59,19 +59,23 @@ def n_protected(L):
     return min(L, 4) + max(0, min(128, L - 4)) if L > 0 else 0
 
 
-def algorithmic_bytes(fmt, lens, H):
+def algorithmic_bytes(fmt, lens, H, nq=1):
     """Bytes the decode call must move: packed history of unprotected tokens,
-    bf16 rows of protected ones, queries, outputs, block-table entries."""
+    bf16 rows of protected ones, queries, outputs, block-table entries
+    (nq queries of H heads per sequence)."""
     kv = sum((L - n_protected(L)) * TOKEN_BYTES[fmt] + n_protected(L) * ROW_BYTES for L in lens)
     B = len(lens)
-    q = B * H * 576 * 2
-    out = B * H * 513 * 4
+    q = B * nq * H * 576 * 2
+    out = B * nq * H * 513 * 4
     bt = sum(-(-L // PAGE) * 4 for L in lens)
     return kv + q + out + bt
 
 
-def algorithmic_flops(lens, H):
-    return sum(lens) * H * 2 * (576 + 512)
+def algorithmic_flops(lens, H, nq=1):
+    """Score and aggregation FLOPs: query j of a length-L sequence sees
+    L - nq + 1 + j tokens."""
+    seen = sum(max(0, L - nq + 1 + j) for L in lens for j in range(nq))
+    return seen * H * 2 * (576 + 512)
 
 
 def kernel_source_hash():
@@ -98,8 +102,10 @@ def stored_traffic(workload):
 # --------------------------------------------------------------- workload ---
 def upload(ops, torch, d, fmt, dev):
     """Page pool + protection buffers filled through kv_quant_append with the
-    first L_b - 1 tokens of every sequence (the L_b-th is the step's token)."""
+    first L_b - nq tokens of every sequence (the last nq are the step's new
+    tokens, nq = queries per sequence)."""
     B = d.B
+    nq = d.wl.queries
     pb = ops.mla_lb_page_bytes(fmt)
     pages = torch.zeros((d.num_pages, pb), dtype=torch.uint8, device=dev)
     prot = torch.zeros((B, PROT_ROWS, 576), dtype=torch.int16, device=dev)
@@ -109,7 +115,7 @@ def upload(ops, torch, d, fmt, dev):
 
     seq_slot = torch.arange(B, dtype=torch.int32, device=dev)
     for b in range(B):
-        L = int(d.lens[b]) - 1
+        L = int(d.lens[b]) - nq
         if L <= 0:
             continue
         P = np.arange(L, dtype=np.int64)
@@ -119,23 +125,25 @@ def upload(ops, torch, d, fmt, dev):
             torch.full((L,), b, dtype=torch.int32, device=dev),
             torch.from_numpy(P.astype(np.int32)).to(dev),
             torch.full((L,), L, dtype=torch.int32, device=dev), pages, prot)
-    # the step's own token per sequence: position L_b - 1, sequence length L_b
-    lastpos = (d.lens.astype(np.int64) - 1)
+    # the step's own tokens per sequence: positions L_b - nq .. L_b - 1,
+    # sequence length L_b (sequence-major, nq per sequence)
+    newpos = [np.arange(int(d.lens[b]) - nq, int(d.lens[b]), dtype=np.int64) for b in range(B)]
     step = {
-        "latent": i16(np.stack([d.c[b][lastpos[b]] for b in range(B)])),
-        "k_rope": i16(np.stack([d.kr[b][lastpos[b]] for b in range(B)])),
-        "slot": torch.from_numpy(np.array([d.slots(b, [lastpos[b]])[0] for b in range(B)],
-                                          dtype=np.int64)).to(dev),
-        "seq_slot": seq_slot,
-        "pos": torch.from_numpy(lastpos.astype(np.int32)).to(dev),
-        "new_len": torch.from_numpy(d.lens.astype(np.int32)).to(dev),
+        "latent": i16(np.concatenate([d.c[b][newpos[b]] for b in range(B)])),
+        "k_rope": i16(np.concatenate([d.kr[b][newpos[b]] for b in range(B)])),
+        "slot": torch.from_numpy(np.concatenate([d.slots(b, newpos[b]) for b in range(B)])).to(dev),
+        "seq_slot": torch.from_numpy(np.repeat(np.arange(B, dtype=np.int32), nq)).to(dev),
+        "pos": torch.from_numpy(np.concatenate(newpos).astype(np.int32)).to(dev),
+        "new_len": torch.from_numpy(np.repeat(d.lens.astype(np.int32), nq)).to(dev),
     }
     torch.cuda.synchronize()
     return {
         "pages": pages, "prot": prot, "seq_slot": seq_slot,
         "block_table": torch.from_numpy(d.block_table).to(dev),
         "seq_lens": torch.from_numpy(d.lens.astype(np.int32)).to(dev),
-        "q_lat": i16(d.q_lat), "q_rope": i16(d.q_rope), "step": step,
+        "q_lat": i16(d.q_lat).view(B, nq, d.H, 512) if nq > 1 else i16(d.q_lat),
+        "q_rope": i16(d.q_rope).view(B, nq, d.H, 64) if nq > 1 else i16(d.q_rope),
+        "step": step,
     }
 
 
@@ -170,7 +178,13 @@ def cpu_baseline(d, fmt, budget_s=12.0):
     while True:
         b = nseq % d.B
         L = int(d.lens[b])
-        attention.decode_sequence(d.c[b][:L], d.kr[b][:L], d.q_lat[b], d.q_rope[b], fmt, d.scale)
+        nq = d.wl.queries
+        if nq > 1:
+            attention.decode_multi(d.c[b][:L], d.kr[b][:L], d.q_lat[b].reshape(nq, d.H, 512),
+                                   d.q_rope[b].reshape(nq, d.H, 64), fmt, d.scale)
+        else:
+            attention.decode_sequence(d.c[b][:L], d.kr[b][:L], d.q_lat[b], d.q_rope[b], fmt,
+                                      d.scale)
         tokens += L
         nseq += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -179,7 +193,8 @@ def cpu_baseline(d, fmt, budget_s=12.0):
     return {"value": round(tokens / dt, 1), "unit": "KV-tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{nseq} sequence decodes cycling over the {d.B} sequences of the same "
-                      f"workload ({tokens} KV tokens, {d.H} heads): fp32 quantize/dequant of "
+                      f"workload ({tokens} KV tokens, {d.wl.queries} x {d.H} query rows): fp32 "
+                      f"quantize/dequant of "
                       f"every token + fp64 attention, {dt:.1f} s on {threads} BLAS threads"}
 
 
@@ -221,7 +236,10 @@ def main():
     d = synth.draw(wl, extra_tokens=0)
     lens = [int(x) for x in d.lens]
     B, H = d.B, d.H
+    nq = wl.queries
     max_len = max(lens)
+    if nq > 1 and args.step == "fused":
+        args.step = "separate"        # the fused writer serves one new token per sequence
 
     log("uploading + filling cache through kv_quant_append")
     base = upload(ops, torch, d, fmt, dev)
@@ -231,11 +249,12 @@ def main():
     torch.cuda.synchronize()
     log(f"replicas {R} x {fp / 2**20:.1f} MiB")
 
-    ws_bytes = ops.mla_decode_lowbit_workspace(fmt, B, H, max_len, args.splits)
+    ws_bytes = ops.mla_decode_lowbit_mq_workspace(fmt, B, nq, H, max_len, args.splits)
+    oshape = (B, nq, H) if nq > 1 else (B, H)
     for r in reps:
         r["ws"] = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-        r["out"] = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
-        r["lse"] = torch.empty((B, H), dtype=torch.float32, device=dev)
+        r["out"] = torch.empty(oshape + (512,), dtype=torch.float32, device=dev)
+        r["lse"] = torch.empty(oshape, dtype=torch.float32, device=dev)
 
     stream = torch.cuda.Stream()   # default priority
 
@@ -245,10 +264,10 @@ def main():
                             s["new_len"], r["pages"], r["prot"], stream=stream)
 
     def do_decode(r):
-        ops.mla_decode_lowbit(fmt, r["q_lat"], r["q_rope"], r["pages"], r["prot"], r["seq_slot"],
-                              r["block_table"], r["seq_lens"], max_len, d.scale, args.splits,
-                              workspace=r["ws"] if ws_bytes else None, out=r["out"],
-                              lse=r["lse"], stream=stream)
+        fn = ops.mla_decode_lowbit_mq if nq > 1 else ops.mla_decode_lowbit
+        fn(fmt, r["q_lat"], r["q_rope"], r["pages"], r["prot"], r["seq_slot"],
+           r["block_table"], r["seq_lens"], max_len, d.scale, args.splits,
+           workspace=r["ws"] if ws_bytes else None, out=r["out"], lse=r["lse"], stream=stream)
 
     def do_fused(r):
         s = r["step"]
@@ -326,8 +345,8 @@ def main():
         ev1.record(stream)
     ev1.synchronize()
     dec_ms = ev0.elapsed_time(ev1) / args.steps
-    ab = algorithmic_bytes(fmt, lens, H)
-    fl = algorithmic_flops(lens, H)
+    ab = algorithmic_bytes(fmt, lens, H, nq)
+    fl = algorithmic_flops(lens, H, nq)
     achieved_gbs = ab / (dec_ms * 1e-3) / 1e9
     achieved_tflops = fl / (dec_ms * 1e-3) / 1e12
     # which roof binds: bytes at 8 TB/s vs flops at 2.5 PF
@@ -339,8 +358,9 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)}
     roof["traffic"] = stored_traffic(wl.name)
-    roof["kernel"] = ("mla_decode_lowbit (decode128_kernel + combine_kernel)" if H % 128 == 0
-                      else "mla_decode_lowbit (decode16w_kernel + combine_kernel)")
+    entry = "mla_decode_lowbit_mq" if nq > 1 else "mla_decode_lowbit"
+    roof["kernel"] = (f"{entry} (decode128_kernel + combine_kernel)" if (nq * H) % 128 == 0
+                      else f"{entry} (decode16w_kernel + combine_kernel)")
     roof["algorithmic_bytes_per_launch"] = ab
     roof["algorithmic_flops_per_launch"] = fl
     roof["launch_ms"] = round(dec_ms, 5)
@@ -360,13 +380,13 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "format": fmt, "batch": B, "heads": H,
+        "config": {"workload": wl.name, "format": fmt, "batch": B, "heads": H, "queries": nq,
                    "context": [min(lens), max(lens)], "page_tokens": PAGE,
                    "d_c": 512, "d_r": 64, "sink": 4, "recent": 128, "replicas": R,
                    "hip_graph": use_graph, "parallelism": "split-kv on 1 GPU",
                    "step": ("mla_decode_lowbit_append (writer of the B new tokens fused "
                             "into the decode launch)" if args.step == "fused" else
-                            "kv_quant_append(B tokens) + mla_decode_lowbit")},
+                            f"kv_quant_append({nq if nq > 1 else ''}B tokens) + {entry}")},
         "roofline": roof,
         "decode_kv_tokens_per_s": round(kv_tokens / (dec_ms * 1e-3), 1),
         "append_ms": round(app_ms, 5),

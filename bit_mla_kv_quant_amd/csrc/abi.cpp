@@ -111,13 +111,16 @@ int decode_entry(int f, const uint16_t* q_lat, const uint16_t* q_rope, const uin
                  const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t H,
                  float softmax_scale, int32_t num_splits, void* workspace,
                  size_t workspace_bytes, float* out, float* lse, void* stream,
-                 const uint16_t* new_c, const uint16_t* new_r) {
+                 const uint16_t* new_c, const uint16_t* new_r, int32_t nq = 1) {
   if (mlb::page_bytes_of(f) == 0) return MLA_LB_EFORMAT;
   if (!q_lat || !q_rope || !pages || !prot || !seq_slot || !block_table || !seq_lens || !out ||
       !lse)
     return MLA_LB_EINVAL;
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return MLA_LB_EINVAL;
   if (B < 1 || H < 16 || H > MLA_LB_MAX_HEADS || H % 16 != 0) return MLA_LB_ESHAPE;
+  if (nq < 1 || static_cast<int64_t>(nq) * H > MLA_LB_MAX_ROWS) return MLA_LB_ESHAPE;
+  const int32_t hq = H;
+  H = nq * hq;                                       // query rows per sequence
   if (max_seq_len < 0 || max_blocks < 1 || num_pages < 1 || num_seq_slots < 1 || num_splits < 0)
     return MLA_LB_ESHAPE;
   if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks) * 64)
@@ -142,6 +145,8 @@ int decode_entry(int f, const uint16_t* q_lat, const uint16_t* q_rope, const uin
   a.max_seq_len = max_seq_len;
   a.B = B;
   a.H = H;
+  a.nq = nq;
+  a.hq = hq;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.pps = plan.pps;
   a.nsplit = plan.nsplit;
@@ -184,6 +189,30 @@ int mla_decode_lowbit_append(int f, const uint16_t* latent, const uint16_t* k_ro
   return decode_entry(f, q_lat, q_rope, pages, num_pages, prot, num_seq_slots, seq_slot,
                       block_table, max_blocks, seq_lens, max_seq_len, B, H, softmax_scale,
                       num_splits, workspace, workspace_bytes, out, lse, stream, latent, k_rope);
+}
+
+int mla_decode_lowbit_mq_workspace(int f, int32_t B, int32_t nq, int32_t H,
+                                   int32_t max_seq_len, int32_t num_splits, size_t* bytes) {
+  if (mlb::page_bytes_of(f) == 0) return MLA_LB_EFORMAT;
+  if (!bytes) return MLA_LB_EINVAL;
+  if (B < 1 || H < 16 || H > MLA_LB_MAX_HEADS || H % 16 != 0 || nq < 1 ||
+      static_cast<int64_t>(nq) * H > MLA_LB_MAX_ROWS || max_seq_len < 0 || num_splits < 0)
+    return MLA_LB_ESHAPE;
+  *bytes = mlb::make_plan(B, nq * H, max_seq_len, num_splits).ws_bytes;
+  return MLA_LB_OK;
+}
+
+int mla_decode_lowbit_mq(int f, const uint16_t* q_lat, const uint16_t* q_rope,
+                         const uint8_t* pages, int64_t num_pages, const uint16_t* prot,
+                         int32_t num_seq_slots, const int32_t* seq_slot,
+                         const int32_t* block_table, int32_t max_blocks,
+                         const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t nq,
+                         int32_t H, float softmax_scale, int32_t num_splits, void* workspace,
+                         size_t workspace_bytes, float* out, float* lse, void* stream) {
+  return decode_entry(f, q_lat, q_rope, pages, num_pages, prot, num_seq_slots, seq_slot,
+                      block_table, max_blocks, seq_lens, max_seq_len, B, H, softmax_scale,
+                      num_splits, workspace, workspace_bytes, out, lse, stream, nullptr, nullptr,
+                      nq);
 }
 
 int mla_lb_dequant_dump(int f, const uint8_t* pages, int64_t num_pages, int64_t page_id,

@@ -97,6 +97,9 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
     return;
   }
   const int np = p1 - p0;
+  // tokens the lane's row attends to: the causal prefix of its query, all L
+  // when there is one query per sequence
+  const int L_row = L - (a.nq - 1 - head / a.hq);
   // fused writer: the first split of head block 0 stores the newest token
   const bool fused = a.new_c != nullptr;
   if (fused && j == 0 && hb == 0)
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int i = i_base + 8 * (r >> 2) + (r & 3);
-        sacc[r] = (phys >= 0 && i < L) ? sacc[r] * a.scale_log2 : -INFINITY;
+        sacc[r] = (phys >= 0 && i < L_row) ? sacc[r] * a.scale_log2 : -INFINITY;
       }
       float tm = sacc[0];
 #pragma unroll

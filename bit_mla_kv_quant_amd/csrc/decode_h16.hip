@@ -103,6 +103,9 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
     return;
   }
   const int nquart = 4 * (p1 - p0);                // quarter pages of the split
+  // tokens the lane's row (query row 16hg + n16) attends to: the causal
+  // prefix of its query, all L when there is one query per sequence
+  const int L_row = L - (a.nq - 1 - (16 * hg + n16) / a.hq);
   // fused writer: the first split of head group 0 stores the newest token
   const bool fused = a.new_c != nullptr;
   if (fused && j == 0 && hg == 0) fused_append<F>(a, b, L, sq, wave, NW, lane);
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int i = i0 + 4 * g + v;
-      x[v] = (phys >= 0 && i < L) ? sc[v] * a.scale_log2 : -INFINITY;
+      x[v] = (phys >= 0 && i < L_row) ? sc[v] * a.scale_log2 : -INFINITY;
     }
     const float tm = head_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
     // first live quarter of the head sets its reference (all earlier weights

@@ -33,7 +33,9 @@ struct DecodeArgs {
   int32_t max_blocks;
   const int32_t* seq_lens;
   int32_t max_seq_len;   // host bound, already min(max_seq_len, max_blocks*64)
-  int32_t B, H;
+  int32_t B, H;          // H: query rows per sequence (nq queries x hq heads)
+  int32_t nq, hq;        // queries per sequence and heads per query: row r is
+                         // query r / hq, which sees the first L - (nq-1-r/hq) tokens
   float scale_log2;      // softmax_scale * log2(e)
   int32_t pps;           // pages per split
   int32_t nsplit;        // splits of a max_seq_len sequence (grid.x)

@@ -49,6 +49,10 @@ def _load():
         "mla_decode_lowbit_append": (ctypes.c_int, [ctypes.c_int, P, P, P, P, P, I64, P, I32, P,
                                                     P, I32, P, I32, I32, I32, F, I32, P, SZ, P,
                                                     P, P]),
+        "mla_decode_lowbit_mq_workspace": (ctypes.c_int, [ctypes.c_int, I32, I32, I32, I32, I32,
+                                                          ctypes.POINTER(SZ)]),
+        "mla_decode_lowbit_mq": (ctypes.c_int, [ctypes.c_int, P, P, P, I64, P, I32, P, P, I32, P,
+                                                I32, I32, I32, I32, F, I32, P, SZ, P, P, P]),
         "mla_lb_dequant_dump": (ctypes.c_int, [ctypes.c_int, P, I64, I64, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -63,7 +67,8 @@ _lib = _load()
 # Names the header declares (checked by the ABI tests).
 EXPORTED = ("mla_lb_version", "mla_lb_strerror", "mla_lb_page_bytes",
             "mla_lb_prot_bytes_per_seq", "kv_quant_append", "mla_decode_lowbit_workspace",
-            "mla_decode_lowbit", "mla_decode_lowbit_append", "mla_lb_dequant_dump")
+            "mla_decode_lowbit", "mla_decode_lowbit_append", "mla_decode_lowbit_mq_workspace",
+            "mla_decode_lowbit_mq", "mla_lb_dequant_dump")
 
 
 def raw():
@@ -195,6 +200,43 @@ def mla_decode_lowbit_append(fmt, latent, k_rope, q_lat, q_rope, pages, prot, se
         None if workspace is None else ctypes.c_void_p(workspace.data_ptr()), ws_bytes,
         _ptr(out, (torch.float32,), "out"), _ptr(lse, (torch.float32,), "lse"), _stream(stream))
     _check("mla_decode_lowbit_append", code)
+    return out, lse
+
+
+def mla_decode_lowbit_mq_workspace(fmt, B, nq, H, max_seq_len, num_splits=0):
+    n = ctypes.c_size_t(0)
+    _check("mla_decode_lowbit_mq_workspace",
+           _lib.mla_decode_lowbit_mq_workspace(_fmt(fmt), B, nq, H, max_seq_len, num_splits,
+                                               ctypes.byref(n)))
+    return n.value
+
+
+def mla_decode_lowbit_mq(fmt, q_lat, q_rope, pages, prot, seq_slot, block_table, seq_lens,
+                         max_seq_len, softmax_scale, num_splits=0, workspace=None, out=None,
+                         lse=None, stream=None):
+    """Attention of the last nq tokens of each sequence over their causal
+    prefixes.  q_lat [B,nq,H,512], q_rope [B,nq,H,64] bf16; returns
+    (out fp32 [B,nq,H,512], lse fp32 [B,nq,H])."""
+    B, nq, H = q_lat.shape[0], q_lat.shape[1], q_lat.shape[2]
+    dev = q_lat.device
+    if out is None:
+        out = torch.empty((B, nq, H, 512), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, nq, H), dtype=torch.float32, device=dev)
+    need = mla_decode_lowbit_mq_workspace(fmt, B, nq, H, max_seq_len, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    code = _lib.mla_decode_lowbit_mq(
+        _fmt(fmt), _ptr(q_lat, _BF16, "q_lat"), _ptr(q_rope, _BF16, "q_rope"),
+        _ptr(pages, (torch.uint8,), "pages"), pages.shape[0], _ptr(prot, _BF16, "prot"),
+        prot.shape[0], _ptr(seq_slot, (torch.int32,), "seq_slot"),
+        _ptr(block_table, (torch.int32,), "block_table"), block_table.shape[1],
+        _ptr(seq_lens, (torch.int32,), "seq_lens"), int(max_seq_len), B, nq, H,
+        float(softmax_scale), int(num_splits),
+        None if workspace is None else ctypes.c_void_p(workspace.data_ptr()), ws_bytes,
+        _ptr(out, (torch.float32,), "out"), _ptr(lse, (torch.float32,), "lse"), _stream(stream))
+    _check("mla_decode_lowbit_mq", code)
     return out, lse
 
 

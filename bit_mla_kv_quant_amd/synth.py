@@ -18,10 +18,11 @@ seed is given; the draw order is fixed and listed in ``draw``):
 * content latent c = bf16(N(0,1) * a), drawn sequence by sequence;
 * RoPE key: N(0,1) rotated to the token's position with base 10000 and
   interleaved pairs (2p, 2p+1), angle = pos * 10000^(-2p/64), then bf16;
-* queries q_lat [H,512] and q_rope [H,64] ~ N(0, sd = 1/sqrt(192)), bf16;
+* queries q_lat [H,512] and q_rope [H,64] ~ N(0, sd = 1/sqrt(192)), bf16,
+  one set per query of the sequence (queries x H rows, query-major);
 * softmax scale 1/sqrt(192).
 
-The five named workloads mirror the shapes the method is evaluated on
+The named workloads mirror the shapes the method is evaluated on
 (DeepSeek-V2-Lite-shaped: 16 heads; DeepSeek-V2-shaped: 128 heads; d_c = 512,
 d_R = 64, 64-token pages).  No public dataset is involved.
 """
@@ -48,6 +49,7 @@ class Workload:
     n_outliers: int = 4
     append_steps: int = 0    # decode steps with one appended token per sequence
     seed: int = 0
+    queries: int = 1         # new tokens per sequence that each ask a query
 
     @property
     def ragged(self):
@@ -64,6 +66,10 @@ WORKLOADS = {
                 append_steps=8, seed=20264),
     # the V2-Lite shape in the fp32-RoPE-metadata format [QuantMLA App. C.4/C.5]
     5: Workload("v2lite_c4r4f_b32_h16_l8k", "C4R4F", 32, 16, 8192, 8192, seed=20265),
+    # the V2-Lite shape with 8 new tokens per sequence, each asking a query
+    # (a speculative-decoding verify step or a chunked-prefill tail)
+    6: Workload("v2lite_c4r4_b32_h16_l8k_q8", "C4R4", 32, 16, 8192, 8192, seed=20266,
+                queries=8),
 }
 
 SOFTMAX_SCALE = 1.0 / math.sqrt(192.0)
@@ -100,8 +106,8 @@ class Draw:
     num_pages: int
     c: list                     # per sequence uint16 [L_b + steps, 512]
     kr: list                    # per sequence uint16 [L_b + steps, 64]
-    q_lat: np.ndarray           # uint16 [B, H, 512]
-    q_rope: np.ndarray          # uint16 [B, H, 64]
+    q_lat: np.ndarray           # uint16 [B, queries * H, 512] (query-major rows)
+    q_rope: np.ndarray          # uint16 [B, queries * H, 64]
     scale: float = SOFTMAX_SCALE
 
     @property
@@ -153,15 +159,18 @@ def draw(wl, seed=None, lens=None, extra_tokens=None, shuffle_pages=True, spare_
         kr = rope_rotate(rng.standard_normal((n, D_R)), np.arange(n))
         cs.append(to_bf16_bits(c))
         krs.append(to_bf16_bits(kr))
-    q_lat = to_bf16_bits(rng.normal(0.0, QUERY_SD, size=(B, H, D_C)))
-    q_rope = to_bf16_bits(rng.normal(0.0, QUERY_SD, size=(B, H, D_R)))
+    # query rows: queries x heads per sequence, query-major
+    R = wl.queries * H
+    q_lat = to_bf16_bits(rng.normal(0.0, QUERY_SD, size=(B, R, D_C)))
+    q_rope = to_bf16_bits(rng.normal(0.0, QUERY_SD, size=(B, R, D_R)))
     return Draw(wl=wl, lens=lens.astype(np.int32), block_table=bt, num_pages=total,
                 c=cs, kr=krs, q_lat=q_lat, q_rope=q_rope)
 
 
 def small(fmt="C4R4", batch=2, heads=16, lens=(200, 77), seed=1, outlier_factor=8.0,
-          extra_tokens=0, spare_pages=0, shuffle_pages=True):
+          extra_tokens=0, spare_pages=0, shuffle_pages=True, queries=1):
     """A small ad-hoc workload for tests (explicit lengths)."""
-    wl = Workload("small", fmt, batch, heads, 0, 0, outlier_factor=outlier_factor, seed=seed)
+    wl = Workload("small", fmt, batch, heads, 0, 0, outlier_factor=outlier_factor, seed=seed,
+                  queries=queries)
     return draw(wl, lens=np.asarray(lens), extra_tokens=extra_tokens,
                 spare_pages=spare_pages, shuffle_pages=shuffle_pages)

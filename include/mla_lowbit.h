@@ -86,7 +86,8 @@ enum {
   MLA_LB_D_R = 64,         /* RoPE key width        [MLA blog §3]      */
   MLA_LB_PAGE_TOKENS = 64, /* tokens per page       [QuantMLA App. C.5] */
   MLA_LB_PROT_ROWS = 132,  /* 4 sink + 128 recent   [QuantMLA App. C.5] */
-  MLA_LB_MAX_HEADS = 128
+  MLA_LB_MAX_HEADS = 128,
+  MLA_LB_MAX_ROWS = 1024   /* queries x heads per sequence (mla_decode_lowbit_mq) */
 };
 
 /* Library ABI version (host, pure). */
@@ -218,6 +219,48 @@ int mla_decode_lowbit_append(int f, const uint16_t* latent, const uint16_t* k_ro
                              int32_t B, int32_t H, float softmax_scale, int32_t num_splits,
                              void* workspace, size_t workspace_bytes, float* out, float* lse,
                              void* stream);
+
+/*
+ * mla_decode_lowbit_mq_workspace -- bytes of workspace mla_decode_lowbit_mq
+ * needs for the same (f, B, nq, H, max_seq_len, num_splits) (host, pure).
+ *   bytes (host out)
+ */
+int mla_decode_lowbit_mq_workspace(int f, int32_t B, int32_t nq, int32_t H,
+                                   int32_t max_seq_len, int32_t num_splits, size_t* bytes);
+
+/*
+ * mla_decode_lowbit_mq -- attention of nq consecutive new tokens per sequence
+ * over the mixed-precision cache (several queries per sequence: a verify step
+ * of speculative decoding, or the tail of a chunked prefill -- the
+ * compute-friendly side of MLA attention [MLA blog §7]).  The nq tokens are
+ * the last nq of the sequence and are already in the cache (written by
+ * kv_quant_append with new_len = seq_lens[b]).  For L = seq_lens[b], query j
+ * (position L - nq + j) attends to its causal prefix [MLA blog §8], tokens
+ * [0, L - nq + 1 + j):
+ *
+ *   S[b,j,h,i] = softmax_scale * (q_lat[b,j,h] . c~_i + q_rope[b,j,h] . k~_R,i)
+ *   out[b,j,h] = sum_i softmax_i(S[b,j,h,:]) c~_i,   lse[b,j,h] = ln sum_i e^S
+ *
+ * with (c~_i, k~_R,i) read as in mla_decode_lowbit for a sequence of length
+ * L: the protected set is that of L [QuantMLA §3.3, App. C.5] for every
+ * query of the call (the cache holds no other state).  nq = 1 is exactly
+ * mla_decode_lowbit.  The nq*H query rows share each reconstructed page; when
+ * nq*H is a multiple of 128 the 128-row matrix-core kernel runs.
+ *
+ *   q_lat  [B][nq][H][512] bf16,  q_rope [B][nq][H][64] bf16
+ *   nq >= 1 with nq*H <= MLA_LB_MAX_ROWS; H as in mla_decode_lowbit
+ *   out    [B][nq][H][512] fp32,  lse [B][nq][H] fp32 (a query whose prefix
+ *          is empty, L - nq + 1 + j <= 0, gets out 0 and lse -inf)
+ *   workspace: at least mla_decode_lowbit_mq_workspace(...) bytes
+ *   other arguments and errors: as mla_decode_lowbit.
+ */
+int mla_decode_lowbit_mq(int f, const uint16_t* q_lat, const uint16_t* q_rope,
+                         const uint8_t* pages, int64_t num_pages, const uint16_t* prot,
+                         int32_t num_seq_slots, const int32_t* seq_slot,
+                         const int32_t* block_table, int32_t max_blocks,
+                         const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t nq,
+                         int32_t H, float softmax_scale, int32_t num_splits, void* workspace,
+                         size_t workspace_bytes, float* out, float* lse, void* stream);
 
 /*
  * mla_lb_dequant_dump -- write the bf16 rows the decode kernel reconstructs

@@ -89,6 +89,20 @@ class GpuCache:
         torch.cuda.synchronize()
         return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
+    def decode_mq(self, lens=None, num_splits=0, max_seq_len=None):
+        """mla_decode_lowbit_mq over the drawn query rows: [B, queries, H, ...]."""
+        d = self.d
+        nq, H = d.wl.queries, d.H
+        lens = self.lens if lens is None else np.asarray(lens)
+        msl = int(lens.max()) if max_seq_len is None else max_seq_len
+        ql = t_bf16(d.q_lat).view(d.B, nq, H, 512)
+        qr = t_bf16(d.q_rope).view(d.B, nq, H, 64)
+        out, lse = self.ops.mla_decode_lowbit_mq(
+            self.fmt, ql, qr, self.pages, self.prot, self.seq_slot, self.block_table,
+            t_i32(lens), msl, d.scale, num_splits=num_splits)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
     def fused_step(self, lens, num_splits=0, max_seq_len=None):
         """mla_decode_lowbit_append: store token lens[b]-1 of each sequence
         (lens[b] > 0) and decode over lens[b] tokens, in one call."""
@@ -120,6 +134,12 @@ class GpuCache:
 def oracle_decode(d, b, L, fmt=None):
     return attention.decode_sequence(d.c[b][:L], d.kr[b][:L], d.q_lat[b], d.q_rope[b],
                                      fmt or d.wl.fmt, d.scale)
+
+
+def oracle_decode_mq(d, b, L, fmt=None):
+    nq, H = d.wl.queries, d.H
+    return attention.decode_multi(d.c[b][:L], d.kr[b][:L], d.q_lat[b].reshape(nq, H, 512),
+                                  d.q_rope[b].reshape(nq, H, 64), fmt or d.wl.fmt, d.scale)
 
 
 def oracle_page(d, pid, lens, fmt=None):

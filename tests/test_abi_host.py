@@ -126,6 +126,29 @@ def test_fused_step_validation(ops):
     assert call(ns=2, ws=FAKE, ws_bytes=need - 1) == -4
 
 
+def test_multi_query_validation(ops):
+    lib = ops.raw()
+
+    def call(f=0, nq=4, H=16, scale=0.07, ns=0, ws=None, ws_bytes=0, q_lat=FAKE):
+        return lib.mla_decode_lowbit_mq(f, q_lat, FAKE, FAKE, 8, FAKE, 2, FAKE, FAKE, 4, FAKE,
+                                        200, 2, nq, H, scale, ns, ws, ws_bytes, FAKE, FAKE, None)
+    assert call(f=3) == -3
+    assert call(q_lat=None) == -1
+    assert call(scale=0.0) == -1
+    for nq in (0, -1, 9):                  # 9 x 128 rows > MLA_LB_MAX_ROWS
+        assert call(nq=nq, H=128) == -2, nq
+    assert call(nq=65, H=16) == -2
+    assert call(H=24) == -2
+    need = ops.mla_decode_lowbit_mq_workspace("C4R4", 2, 4, 16, 200, 2)
+    assert need == 2 * 2 * 64 * 516 * 4
+    assert need == ops.mla_decode_lowbit_workspace("C4R4", 2, 64, 200, 2)
+    assert call(ns=2) == -4
+    assert call(ns=2, ws=FAKE, ws_bytes=need - 1) == -4
+    with pytest.raises(ops.MlaLowbitError):
+        ops.mla_decode_lowbit_mq_workspace("C4R4", 1, 0, 16, 100, 0)
+    assert ops.mla_decode_lowbit_mq_workspace("C4R4", 1, 8, 128, 100000, 0) > 0
+
+
 def test_dequant_dump_validation(ops):
     lib = ops.raw()
     assert lib.mla_lb_dequant_dump(3, FAKE, 4, 0, FAKE, None) == -3

@@ -12,7 +12,7 @@ import pytest
 from bit_mla_kv_quant_amd import synth
 from oracle import attention, layout, quant
 
-from gpu_helpers import GpuCache, oracle_decode, oracle_page, rel_l2
+from gpu_helpers import GpuCache, oracle_decode, oracle_decode_mq, oracle_page, rel_l2
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -261,6 +261,56 @@ def test_fused_token_aging(fmt):
     pages = c.pages.cpu().numpy()
     for pid in range(d.num_pages):
         np.testing.assert_array_equal(pages[pid], oracle_page(d, pid, [steps, steps]))
+
+
+# ------------------------------------------------ several queries per sequence ---
+def check_decode_mq(d, out, lse, lens, which=None, fmt=None):
+    worst = 0.0
+    for b in (range(d.B) if which is None else which):
+        L = int(lens[b])
+        ro, rl = oracle_decode_mq(d, b, L, fmt)
+        for j in range(d.wl.queries):
+            if L - d.wl.queries + 1 + j <= 0:      # empty causal prefix
+                assert np.all(out[b, j] == 0) and np.all(np.isneginf(lse[b, j])), (b, j)
+                continue
+            e = rel_l2(out[b, j], ro[j])
+            worst = max(worst, e)
+            assert e <= TOL_OUT, (b, L, j, e)
+            assert np.max(np.abs(lse[b, j] - rl[j])) <= TOL_LSE, (b, L, j)
+    return worst
+
+
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "C4R4F"])
+@pytest.mark.parametrize("nq,H", [(1, 16), (2, 16), (3, 32), (8, 16), (2, 128)])
+def test_multi_query_decode(fmt, nq, H):
+    """nq queries per sequence, each over its causal prefix, against the
+    oracle; lengths below nq (empty prefixes), at sink / page / window edges
+    and over several splits.  8 x 16 and 2 x 128 rows take the 128-row
+    kernel, the others the 16-row one; nq = 1 must equal mla_decode_lowbit."""
+    lens = np.array([1, 3, 8, 9, 64, 65, 133, 140, 300, 1000])
+    d = synth.small(fmt=fmt, batch=len(lens), heads=H, lens=lens, seed=51 + nq, queries=nq)
+    say("multi_query", fmt, nq, H, lens.tolist())
+    c = GpuCache(d)
+    c.fill()
+    for ns in (0, 1, 3):
+        out, lse = c.decode_mq(num_splits=ns)
+        w = check_decode_mq(d, out, lse, lens)
+        say("  num_splits", ns, "worst rel-L2", f"{w:.2e}")
+        if nq == 1:
+            o1, l1 = c.decode(num_splits=ns)
+            np.testing.assert_array_equal(out[:, 0], o1)
+            np.testing.assert_array_equal(lse[:, 0], l1)
+
+
+def test_config6_multi_query_v2lite():
+    wl = synth.WORKLOADS[6]
+    say("config 6", wl.name, "drawing")
+    d = synth.draw(wl)
+    c = GpuCache(d)
+    c.fill()
+    out, lse = c.decode_mq()
+    w = check_decode_mq(d, out, lse, d.lens, which=[0, 31])
+    say("config 6 worst rel-L2 on sampled sequences", f"{w:.2e}")
 
 
 def _slot_regions(fmt, off):
