@@ -100,10 +100,15 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
   // tokens the lane's row attends to: the causal prefix of its query, all L
   // when there is one query per sequence
   const int L_row = L - (a.nq - 1 - head / a.hq);
-  // fused writer: the first split of head block 0 stores the newest token
   const bool fused = a.new_c != nullptr;
-  if (fused && j == 0 && hb == 0)
-    fused_append<F>(a, b, L, sq, __builtin_amdgcn_readfirstlane(wave), 4, lane);
+  // fused writer: the first split of the first head block stores the newest
+  // token before its page loop (no workgroup of this launch reads those
+  // bytes; this kernel has no registers to spare for holding the row across
+  // the loop)
+  if (fused && j == 0 && hb == 0) {
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    fused_store<F>(a, fused_load(a, b, wv, 4, lane), b, L, sq, wv, 4, lane);
+  }
 
   const __attribute__((address_space(4))) int32_t* bt_row =
       (const __attribute__((address_space(4))) int32_t*)(a.block_table +

@@ -106,9 +106,12 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
   // tokens the lane's row (query row 16hg + n16) attends to: the causal
   // prefix of its query, all L when there is one query per sequence
   const int L_row = L - (a.nq - 1 - (16 * hg + n16) / a.hq);
-  // fused writer: the first split of head group 0 stores the newest token
   const bool fused = a.new_c != nullptr;
-  if (fused && j == 0 && hg == 0) fused_append<F>(a, b, L, sq, wave, NW, lane);
+  // fused writer: the first split of the first head block fetches the
+  // newest token now and stores it once its own work is done
+  const bool writer = fused && j == 0 && hg == 0;
+  FusedRow fresh_row{};
+  if (writer) fresh_row = fused_load(a, b, wave, NW, lane);
 
   const __attribute__((address_space(4))) int32_t* bt_row =
       (const __attribute__((address_space(4))) int32_t*)(a.block_table +
@@ -416,6 +419,7 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
     *(f32x4*)(dst + RD * r + d8 + 4) = o1 * osc;
     __syncthreads();
   }
+  if (writer) fused_store<F>(a, fresh_row, b, L, sq, wave, NW, lane);
 }
 
 int launch_decode16w(int f, const DecodeArgs& a, hipStream_t stream) {

@@ -153,20 +153,38 @@ __device__ __forceinline__ void write_group(uint8_t* pg, int off, int g, uint16_
 // names, and into its protection-buffer row (the newest token is always in
 // the recent window).  The nw waves of the calling workgroup share the nine
 // groups: wave w takes groups w, w + nw, ...  `wave` is wave-uniform.
+// fused_load fetches the wave's values early (so their latency overlaps the
+// decode work); fused_store quantizes and stores them.
+struct FusedRow {
+  uint16_t x[3];                                   // groups wave, wave+nw, wave+2nw
+};
+__device__ __forceinline__ FusedRow fused_load(const DecodeArgs& a, int b, int wave, int nw,
+                                               int lane) {
+  FusedRow r{};
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int g = wave + k * nw;
+    if (g <= NGC)
+      r.x[k] = g < NGC ? a.new_c[(int64_t)b * DC + 64 * g + lane] : a.new_r[(int64_t)b * DR + lane];
+  }
+  return r;
+}
 template <int F>
-__device__ __forceinline__ void fused_append(const DecodeArgs& a, int b, int L, int sq, int wave,
-                                             int nw, int lane) {
+__device__ __forceinline__ void fused_store(const DecodeArgs& a, const FusedRow& r, int b, int L,
+                                            int sq, int wave, int nw, int lane) {
   const int pos = L - 1;
   const int phys = a.block_table[(int64_t)b * a.max_blocks + pos / PAGE];
   if (phys < 0 || phys >= a.num_pages) return;     // unusable table entry: nothing stored
   uint8_t* pg = a.wpages + (int64_t)phys * Fmt<F>::PAGE_BYTES;
   const int off = pos % PAGE;
   uint16_t* dst = a.wprot + ((int64_t)sq * PROT_ROWS + prot_row(pos)) * DROW;
-  for (int g = wave; g <= NGC; g += nw) {
-    const uint16_t x = g < NGC ? a.new_c[(int64_t)b * DC + 64 * g + lane]
-                               : a.new_r[(int64_t)b * DR + lane];
-    write_group<F>(pg, off, g, x, lane);
-    dst[64 * g + lane] = x;                        // g == 8: RoPE dims 512 + lane
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int g = wave + k * nw;
+    if (g <= NGC) {
+      write_group<F>(pg, off, g, r.x[k], lane);
+      dst[64 * g + lane] = r.x[k];                 // g == 8: RoPE dims 512 + lane
+    }
   }
 }
 
