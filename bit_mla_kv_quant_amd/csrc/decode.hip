@@ -33,6 +33,31 @@ __device__ __forceinline__ void combine_term(const f32x4& ml, const f32x4& ov, f
   }
 }
 
+// Up to N splits with every partial in flight at once, then one pass.
+template <int N>
+__device__ __forceinline__ void combine_all(const DecodeArgs& a, int64_t base, int ns, int d0,
+                                            float& M, f32x4& accv, float& ssum, float& fsum) {
+  f32x4 ml[N], ov[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    if (u < ns) {
+      const int64_t e = base + (int64_t)u * a.H;
+      ml[u] = *(const f32x4*)(a.ws_ml + e * 4);
+      ov[u] = *(const f32x4*)(a.ws_o + e * DC + d0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+    if (u < ns) M = fmaxf(M, ml[u][0]);
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+    if (u < ns) combine_term(ml[u], ov[u], M, accv, ssum, fsum);
+}
+
+// NMAX: 8 or 16 for plans of at most that many splits (all loads in flight
+// at once; separate instantiations keep the register count of the common
+// 8-split case low), 0 for longer plans (four splits at a time).
+template <int NMAX>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int b = blockIdx.z, H = a.H;
   const int hh = threadIdx.x >> 4, c = threadIdx.x & 15;
@@ -43,23 +68,8 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int64_t base = (int64_t)b * ns * H + h;          // split jj at base + jj*H
   f32x4 accv = {0.f, 0.f, 0.f, 0.f};
   float ssum = 0.f, fsum = 0.f, M = -INFINITY;
-  if (ns <= 8) {
-    // every partial in flight at once, then one pass
-    f32x4 ml[8], ov[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (u < ns) {
-        const int64_t e = base + (int64_t)u * H;
-        ml[u] = *(const f32x4*)(a.ws_ml + e * 4);
-        ov[u] = *(const f32x4*)(a.ws_o + e * DC + d0);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (u < ns) M = fmaxf(M, ml[u][0]);
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (u < ns) combine_term(ml[u], ov[u], M, accv, ssum, fsum);
+  if constexpr (NMAX > 0) {
+    combine_all<NMAX>(a, base, ns, d0, M, accv, ssum, fsum);
   } else {
     for (int jj = 0; jj < ns; ++jj) M = fmaxf(M, a.ws_ml[(base + (int64_t)jj * H) * 4]);
     int jj = 0;
@@ -115,7 +125,10 @@ int launch_decode(int f, const DecodeArgs& a, hipStream_t stream) {
     if (launch_decode16w(f, a, stream) != 0) return -5;
   }
   if (a.nsplit > 1) {
-    hipLaunchKernelGGL(combine_kernel, dim3(DC / 64, a.H / 16, a.B), dim3(256), 0, stream, a);
+    const dim3 grid(DC / 64, a.H / 16, a.B), block(256);
+    if (a.nsplit <= 8) hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, stream, a);
+    else if (a.nsplit <= 16) hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(combine_kernel<0>, grid, block, 0, stream, a);
     if (hipGetLastError() != hipSuccess) return -5;
   }
   return 0;

@@ -101,11 +101,12 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
   // when there is one query per sequence
   const int L_row = L - (a.nq - 1 - head / a.hq);
   const bool fused = a.new_c != nullptr;
-  // fused writer: the first split of the first head block stores the newest
-  // token before its page loop (no workgroup of this launch reads those
-  // bytes; this kernel has no registers to spare for holding the row across
-  // the loop)
-  if (fused && j == 0 && hb == 0) {
+  // fused writer: the middle split of the sequence (first head block)
+  // stores the newest token before its page loop.  No workgroup of this
+  // launch reads those bytes; a middle split holds neither the sink tokens
+  // nor the recent window, so it has time to spare; and this kernel has no
+  // registers to spare for holding the row across the loop.
+  if (fused && j == (npages + a.pps - 1) / a.pps / 2 && hb == 0) {
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     fused_store<F>(a, fused_load(a, b, wv, 4, lane), b, L, sq, wv, 4, lane);
   }

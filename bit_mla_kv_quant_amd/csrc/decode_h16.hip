@@ -107,9 +107,12 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
   // prefix of its query, all L when there is one query per sequence
   const int L_row = L - (a.nq - 1 - (16 * hg + n16) / a.hq);
   const bool fused = a.new_c != nullptr;
-  // fused writer: the first split of the first head block fetches the
-  // newest token now and stores it once its own work is done
-  const bool writer = fused && j == 0 && hg == 0;
+  // fused writer: the middle split of the sequence (first head block)
+  // fetches the newest token now and stores it once its own work is done.
+  // A middle split holds neither the sink tokens nor the recent window, so
+  // it finishes ahead of the splits that do and the writer hides behind them.
+  const int nsplit_b = (npages + a.pps - 1) / a.pps;
+  const bool writer = fused && j == nsplit_b / 2 && hg == 0;
   FusedRow fresh_row{};
   if (writer) fresh_row = fused_load(a, b, wave, NW, lane);
 

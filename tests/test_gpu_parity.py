@@ -106,6 +106,40 @@ def test_dequant_edge_values(fmt):
     np.testing.assert_array_equal(got, want)
 
 
+@pytest.mark.parametrize("fmt", ["C4R4", "C4R4F"])
+@pytest.mark.parametrize("H", [16, 128])
+def test_decode_huge_scale_groups(fmt, H):
+    """Packed tokens whose content or RoPE group has a scale beyond the fp8
+    conversion's range (s * 2^9 overflows fp32) take the per-code conversion
+    in both decode kernels; the attention still matches the oracle (such a
+    token takes nearly all the weight of heads whose score it dominates)."""
+    d = synth.small(fmt=fmt, batch=2, heads=H, lens=(700, 1300), seed=61)
+    rng = np.random.default_rng(61)
+    c = quant.bf16_to_f32(d.c[0]).copy()
+    c[300, 64:128] = rng.uniform(-1.0, 1.0, 64) * 1e37      # content group 1 of a packed token
+    d.c[0] = quant.f32_to_bf16(c.astype(np.float32))
+    kr = quant.bf16_to_f32(d.kr[1]).copy()
+    kr[900, :] = rng.uniform(-1.0, 1.0, 64) * 1e37          # RoPE group of a packed token
+    d.kr[1] = quant.f32_to_bf16(kr.astype(np.float32))
+    say("huge_scale", fmt, H)
+    g = GpuCache(d)
+    g.fill()
+    for ns in (0, 1):
+        out, lse = g.decode(num_splits=ns)
+        assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+        for b in range(d.B):
+            L = int(d.lens[b])
+            ro, rl = oracle_decode(d, b, L)
+            assert rel_l2(out[b], ro) <= TOL_OUT, (b, rel_l2(out[b], ro))
+            # scores of ~1e35 are fp32 sums of 576 products that cancel: their
+            # error is bounded by gamma_576 * sum |q_j x_j| (gamma_576 < 1e-4),
+            # so the lse bar grows with that magnitude
+            rows = attention.effective_rows(d.c[b][:L], d.kr[b][:L], fmt)
+            q = quant.bf16_to_f32(np.concatenate([d.q_lat[b], d.q_rope[b]], axis=1)).astype(np.float64)
+            mag = d.scale * (np.abs(q) @ np.abs(rows).T).max(axis=1)
+            assert np.all(np.abs(lse[b] - rl) <= TOL_LSE + 1e-4 * mag), b
+
+
 # --------------------------------------------------------------- decode ---
 EDGE_LENS = (0, 1, 3, 4, 5, 63, 64, 65, 127, 128, 129, 131, 132, 133, 200, 1000)
 
