@@ -1,0 +1,87 @@
+"""Pins for oracle/transforms.py (CPU only).
+
+Closed forms and identities: the per-pair rotation/scale commutes with the
+positional rotation of the synthetic keys (an independent routine) and keeps
+q.k; a dense cross-pair rotation does not (negative control).  Power-of-two
+scales make the bf16 cache scaling exact, so the compensated attention
+equals the untransformed one to fp64 rounding.  Hand-computed scales.  A
+measured property: on outlier channels the held-out search picks alpha > 0
+and lowers the attention-output error below plain round-to-nearest.
+"""
+
+import numpy as np
+import pytest
+
+from bit_mla_kv_quant_amd import synth
+from oracle import quant, transforms
+
+
+def test_pair_transform_commutes_with_rope_and_keeps_scores():
+    rng = np.random.default_rng(0)
+    n = 40
+    k = rng.standard_normal((n, 64))
+    q = rng.standard_normal((n, 64))
+    pos = rng.integers(0, 100000, n)
+    ang = rng.uniform(-np.pi, np.pi, 32)
+    sc = np.exp(rng.uniform(-2, 2, 32))
+    # transform before or after the positional rotation: same keys
+    a = synth.rope_rotate(transforms.pair_transform(k, ang, sc), pos)
+    b = transforms.pair_transform(synth.rope_rotate(k, pos), ang, sc)
+    np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-11)
+    # reciprocal compensation keeps every positional score
+    kp = transforms.pair_transform(k, ang, sc)
+    qp = transforms.pair_transform(q, ang, 1.0 / sc)
+    np.testing.assert_allclose(qp @ kp.T, q @ k.T, rtol=1e-11, atol=1e-11)
+    # negative control: a dense rotation across pairs does not commute
+    Q, _ = np.linalg.qr(rng.standard_normal((64, 64)))
+    assert np.max(np.abs(synth.rope_rotate(k @ Q, pos) - synth.rope_rotate(k, pos) @ Q)) > 1e-3
+
+
+def test_smooth_scales_closed_form_and_pair_tying():
+    s = transforms.smooth_scales([4.0, 1.0, 0.0, 16.0], 0.5)
+    np.testing.assert_allclose(s, [0.5, 1.0, 1e4, 0.25], rtol=1e-12)
+    assert np.all(transforms.smooth_scales([4.0, 1.0, 0.0, 16.0], 0.0) == 1.0)
+    sp = transforms.smooth_scales([4.0, 1.0, 0.25, 16.0], 1.0, pairs=True)
+    np.testing.assert_allclose(sp, [0.25, 0.25, 1 / 16, 1 / 16], rtol=1e-12)
+    a = np.abs(np.random.default_rng(1).standard_normal(64)) + 0.1
+    st = transforms.channel_stat(np.stack([a, -a, 0.5 * a]))
+    np.testing.assert_allclose(st, a, rtol=1e-12)
+
+
+def test_scaled_decode_preserves_attention_without_quantization():
+    """All tokens protected (L <= 132): with power-of-two scales the bf16
+    cache scaling is exact, so compensation must give back the untransformed
+    attention to fp64 rounding."""
+    d = synth.small(fmt="C4R4", batch=1, heads=4, lens=(120,), seed=2)
+    rng = np.random.default_rng(2)
+    s_c = 2.0 ** rng.integers(-6, 7, 512)
+    s_r = np.repeat(2.0 ** rng.integers(-6, 7, 32), 2)
+    out, lse = transforms.decode_scaled(d.c[0], d.kr[0], d.q_lat[0], d.q_rope[0], "C4R4",
+                                        d.scale, s_c, s_r)
+    ref, rl = transforms.exact_decode(d.c[0], d.kr[0], d.q_lat[0], d.q_rope[0], d.scale)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, rl, rtol=1e-12, atol=1e-12)
+
+
+def _outlier_draw(seed, L, heads=4):
+    d = synth.small(fmt="C4R4", batch=3, heads=heads, lens=(L, L, L), seed=seed,
+                    outlier_factor=16.0)
+    # RoPE outliers: four frequency pairs x16 in every key
+    kr = [quant.bf16_to_f32(x).copy() for x in d.kr]
+    for x in kr:
+        for p in (3, 10, 17, 29):
+            x[:, 2 * p:2 * p + 2] *= 16.0
+    d.kr = [quant.f32_to_bf16(x.astype(np.float32)) for x in kr]
+    return d
+
+
+@pytest.mark.parametrize("path", ["content", "rope"])
+def test_alpha_search_lowers_error_on_outlier_channels(path):
+    d = _outlier_draw(seed=7, L=700)
+    calib_c, calib_kr = d.c[0], d.kr[0]                  # statistics from sequence 0
+    heldout = [(d.c[b], d.kr[b], d.q_lat[b], d.q_rope[b]) for b in (1, 2)]
+    al, errs, s = transforms.select_alpha(calib_c, calib_kr, heldout, "C4R4", d.scale, path)
+    assert al > 0.0, errs
+    assert errs[al] < 0.9 * errs[0.0], errs
+    if path == "rope":
+        assert np.all(s[0::2] == s[1::2])
