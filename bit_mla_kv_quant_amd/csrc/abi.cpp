@@ -1,8 +1,11 @@
 // C-ABI host layer of libmla_lowbit.so: argument validation (pure host code,
 // runs before any HIP call), the split plan, and dispatch to the kernels.
+#include <algorithm>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <cstring>
+#include <vector>
 
 #include "../../include/mla_lowbit.h"
 #include "internal.h"
@@ -213,6 +216,47 @@ int mla_decode_lowbit_mq(int f, const uint16_t* q_lat, const uint16_t* q_rope,
                       block_table, max_blocks, seq_lens, max_seq_len, B, H, softmax_scale,
                       num_splits, workspace, workspace_bytes, out, lse, stream, nullptr, nullptr,
                       nq);
+}
+
+int mla_lb_channel_stat(const uint16_t* x, int64_t rows, int32_t n, double pct, float* stat) {
+  if (!x || !stat) return MLA_LB_EINVAL;
+  if (rows < 1 || n < 1 || !(pct >= 0.0 && pct <= 100.0)) return MLA_LB_ESHAPE;
+  std::vector<double> col(static_cast<size_t>(rows));
+  // linear interpolation between the order statistics around pct/100*(rows-1)
+  const double posn = pct / 100.0 * static_cast<double>(rows - 1);
+  const int64_t lo = static_cast<int64_t>(std::floor(posn));
+  const int64_t hi = std::min<int64_t>(lo + 1, rows - 1);
+  const double frac = posn - static_cast<double>(lo);
+  for (int32_t j = 0; j < n; ++j) {
+    for (int64_t r = 0; r < rows; ++r) {
+      const uint32_t bits = static_cast<uint32_t>(x[r * n + j]) << 16;
+      float f;
+      std::memcpy(&f, &bits, sizeof f);
+      col[static_cast<size_t>(r)] = std::fabs(static_cast<double>(f));
+    }
+    std::sort(col.begin(), col.end());
+    const double v = col[static_cast<size_t>(lo)] +
+                     (col[static_cast<size_t>(hi)] - col[static_cast<size_t>(lo)]) * frac;
+    stat[j] = static_cast<float>(v);
+  }
+  return MLA_LB_OK;
+}
+
+int mla_lb_smooth_scales(const float* stat, int32_t n, float alpha, int32_t pair_tied,
+                         float* scales) {
+  if (!stat || !scales) return MLA_LB_EINVAL;
+  if (n < 1 || (pair_tied && n % 2 != 0) || !(alpha >= 0.0f) || !std::isfinite(alpha))
+    return MLA_LB_ESHAPE;
+  for (int32_t j = 0; j < n; ++j) {
+    double a = std::max(static_cast<double>(stat[j]), 1e-8);
+    if (pair_tied) {
+      const int32_t p = j & ~1;
+      a = std::max(std::max(static_cast<double>(stat[p]), 1e-8),
+                   std::max(static_cast<double>(stat[p + 1]), 1e-8));
+    }
+    scales[j] = static_cast<float>(std::pow(a, -static_cast<double>(alpha)));
+  }
+  return MLA_LB_OK;
 }
 
 int mla_lb_dequant_dump(int f, const uint8_t* pages, int64_t num_pages, int64_t page_id,

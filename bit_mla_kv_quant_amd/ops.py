@@ -53,6 +53,8 @@ def _load():
                                                           ctypes.POINTER(SZ)]),
         "mla_decode_lowbit_mq": (ctypes.c_int, [ctypes.c_int, P, P, P, I64, P, I32, P, P, I32, P,
                                                 I32, I32, I32, I32, F, I32, P, SZ, P, P, P]),
+        "mla_lb_channel_stat": (ctypes.c_int, [P, I64, I32, ctypes.c_double, P]),
+        "mla_lb_smooth_scales": (ctypes.c_int, [P, I32, F, I32, P]),
         "mla_lb_dequant_dump": (ctypes.c_int, [ctypes.c_int, P, I64, I64, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -68,7 +70,8 @@ _lib = _load()
 EXPORTED = ("mla_lb_version", "mla_lb_strerror", "mla_lb_page_bytes",
             "mla_lb_prot_bytes_per_seq", "kv_quant_append", "mla_decode_lowbit_workspace",
             "mla_decode_lowbit", "mla_decode_lowbit_append", "mla_decode_lowbit_mq_workspace",
-            "mla_decode_lowbit_mq", "mla_lb_dequant_dump")
+            "mla_decode_lowbit_mq", "mla_lb_channel_stat", "mla_lb_smooth_scales",
+            "mla_lb_dequant_dump")
 
 
 def raw():
@@ -238,6 +241,29 @@ def mla_decode_lowbit_mq(fmt, q_lat, q_rope, pages, prot, seq_slot, block_table,
         _ptr(out, (torch.float32,), "out"), _ptr(lse, (torch.float32,), "lse"), _stream(stream))
     _check("mla_decode_lowbit_mq", code)
     return out, lse
+
+
+def mla_lb_channel_stat(x_bits, pct=99.9):
+    """Host helper: per-channel pct-th percentile of |x| for bf16 bits
+    x_bits (numpy uint16/int16 [rows, n]); returns float32 [n]."""
+    import numpy as np
+    x = np.ascontiguousarray(x_bits).view(np.uint16)
+    rows, n = x.shape
+    out = np.empty(n, np.float32)
+    _check("mla_lb_channel_stat",
+           _lib.mla_lb_channel_stat(x.ctypes.data, rows, n, float(pct), out.ctypes.data))
+    return out
+
+
+def mla_lb_smooth_scales(stat, alpha, pair_tied=False):
+    """Host helper: s_j = max(a_j, 1e-8)^-alpha (pairs tied on request)."""
+    import numpy as np
+    a = np.ascontiguousarray(stat, dtype=np.float32)
+    out = np.empty(a.shape[0], np.float32)
+    _check("mla_lb_smooth_scales",
+           _lib.mla_lb_smooth_scales(a.ctypes.data, a.shape[0], float(alpha), int(bool(pair_tied)),
+                                     out.ctypes.data))
+    return out
 
 
 def mla_lb_dequant_dump(fmt, pages, page_id, out=None, stream=None):

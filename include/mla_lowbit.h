@@ -263,6 +263,29 @@ int mla_decode_lowbit_mq(int f, const uint16_t* q_lat, const uint16_t* q_rope,
                          size_t workspace_bytes, float* out, float* lse, void* stream);
 
 /*
+ * Offline calibration helpers (host, pure; no GPU).  The cache transforms
+ * they serve are folded into the model's projections before serving, so the
+ * decode path runs unchanged [QuantMLA App. C.1, C.2, D.2]: a content channel
+ * j is cached as x_j * s_j with queries and the aggregated latent compensated
+ * by 1/s_j; a RoPE frequency pair (2i, 2i+1) shares one scale, with the
+ * reciprocal on the query, which keeps every positional score and commutes
+ * with the positional rotation.
+ *
+ * mla_lb_channel_stat -- per channel j < n, the pct-th percentile of |x[r][j]|
+ *   over rows r < rows (linear interpolation between order statistics),
+ *   x host bf16 [rows][n], stat host fp32 [n].  pct in [0, 100].
+ * mla_lb_smooth_scales -- s_j = max(a_j, 1e-8)^(-alpha) from statistics
+ *   stat[n] (host fp32); pair_tied != 0 gives channels 2i and 2i+1 the
+ *   statistic max(a~_2i, a~_2i+1) (n even).  alpha >= 0; alpha = 0 gives 1.
+ *   The candidate rule is read as the SmoothQuant smoothing factor with
+ *   activation statistics only (the formula is missing from the pages'
+ *   extracted text); alpha is chosen by held-out attention-output error.
+ */
+int mla_lb_channel_stat(const uint16_t* x, int64_t rows, int32_t n, double pct, float* stat);
+int mla_lb_smooth_scales(const float* stat, int32_t n, float alpha, int32_t pair_tied,
+                         float* scales);
+
+/*
  * mla_lb_dequant_dump -- write the bf16 rows the decode kernel reconstructs
  * for every slot of one page, [64][576] = [c^ | k^_R], using the same device
  * code as mla_decode_lowbit.  For checking the reconstruction bit for bit.

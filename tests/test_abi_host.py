@@ -167,3 +167,27 @@ def test_workspace_plan(ops):
         assert n % (B * H * 516 * 4) == 0
     with pytest.raises(ops.MlaLowbitError):
         ops.mla_decode_lowbit_workspace("C4R4", 1, 20, 100, 0)
+
+
+def test_calibration_helpers_match_oracle(ops):
+    """Host calibration helpers (no GPU) against the oracle's fp64 values."""
+    import numpy as np
+    from bit_mla_kv_quant_amd import synth
+    from oracle import transforms, quant
+    d = synth.small(fmt="C4R4", batch=1, heads=16, lens=(777,), seed=4, outlier_factor=16.0)
+    for x in (d.c[0], d.kr[0]):
+        got = ops.mla_lb_channel_stat(x, 99.9)
+        want = transforms.channel_stat(quant.bf16_to_f32(x))
+        np.testing.assert_array_equal(got, want.astype(np.float32))
+        for alpha in (0.0, 0.125, 0.5, 1.0):
+            for pairs in ((False, True) if x.shape[1] == 64 else (False,)):
+                s = ops.mla_lb_smooth_scales(got, alpha, pairs)
+                ws = transforms.smooth_scales(got.astype(np.float64), alpha, pairs)
+                np.testing.assert_allclose(s, ws, rtol=2 ** -23)
+    lib = ops.raw()
+    assert lib.mla_lb_smooth_scales(None, 4, 0.5, 0, FAKE) == -1
+    assert lib.mla_lb_smooth_scales(FAKE, 3, 0.5, 1, FAKE) == -2
+    assert lib.mla_lb_smooth_scales(FAKE, 4, -0.5, 0, FAKE) == -2
+    assert lib.mla_lb_channel_stat(FAKE, 0, 4, 99.9, FAKE) == -2
+    assert lib.mla_lb_channel_stat(FAKE, 4, 4, 101.0, FAKE) == -2
+    assert lib.mla_lb_channel_stat(None, 4, 4, 99.9, FAKE) == -1

@@ -415,3 +415,42 @@ def test_config4_pressure_with_append_steps():
     for b in (0, d.B - 1):
         for pid in np.unique(d.block_table[b, (lens[b] - d.wl.append_steps) // 64:(lens[b] - 1) // 64 + 1]):
             np.testing.assert_array_equal(pages[pid], oracle_page(d, pid, lens))
+
+
+# ------------------------------------------- offline-calibrated cache scales ---
+def test_calibrated_scales_through_kernels():
+    """Statistics-only channel scales (library host helpers) applied to a
+    cache with x16 outlier channels and RoPE pairs, as a model with the
+    scales folded into its projections would produce it; the kernels run
+    unchanged.  The decode of the scaled cache matches the oracle on the
+    same inputs, and after compensation it is closer to full-precision
+    attention than the decode of the unscaled cache."""
+    from bit_mla_kv_quant_amd import ops
+    from oracle import transforms
+    from test_oracle_transforms import _outlier_draw
+    d = _outlier_draw(seed=7, L=700, heads=16)
+    s_c = ops.mla_lb_smooth_scales(ops.mla_lb_channel_stat(d.c[0]), 0.5).astype(np.float64)
+    s_r = ops.mla_lb_smooth_scales(ops.mla_lb_channel_stat(d.kr[0]), 0.75, True).astype(np.float64)
+    say("calibrated scales")
+    plain = GpuCache(d)
+    plain.fill()
+    o_rtn, _ = plain.decode()
+
+    def bf16(x):
+        return quant.f32_to_bf16(np.asarray(x, np.float32))
+    t = synth.small(fmt="C4R4", batch=3, heads=16, lens=tuple(d.lens), seed=7)
+    t.c = [bf16(quant.bf16_to_f32(x) * s_c) for x in d.c]
+    t.kr = [bf16(quant.bf16_to_f32(x) * s_r) for x in d.kr]
+    t.q_lat = bf16(quant.bf16_to_f32(d.q_lat) / s_c)
+    t.q_rope = bf16(quant.bf16_to_f32(d.q_rope) / s_r)
+    t.block_table, t.num_pages = d.block_table, d.num_pages
+    scaled = GpuCache(t)
+    scaled.fill()
+    o_sc, l_sc = scaled.decode()
+    check_decode(t, scaled, o_sc, l_sc, t.lens)          # parity on the scaled inputs
+    for b in (1, 2):                                      # held-out sequences
+        ref, _ = transforms.exact_decode(d.c[b], d.kr[b], d.q_lat[b], d.q_rope[b], d.scale)
+        e_rtn = transforms.nmse(o_rtn[b], ref)
+        e_sc = transforms.nmse(o_sc[b] / s_c, ref)
+        say(f"  seq {b}: NMSE plain {e_rtn:.2e}, scaled {e_sc:.2e}")
+        assert e_sc < e_rtn / 3, (e_rtn, e_sc)
