@@ -259,7 +259,7 @@ def test_fused_step_equals_append_then_decode(fmt, H):
     lens = np.array([1, 4, 5, 64, 65, 132, 133, 300, 1000, 0])
     d = synth.small(fmt=fmt, batch=len(lens), heads=H, lens=lens, seed=41)
     say("fused_step", fmt, H, lens.tolist())
-    base = GpuCache(d)
+    base = GpuCache(d, seq_slots=np.random.default_rng(H).permutation(d.B))
     # every sequence holds its first L-1 tokens
     base.append(list(range(d.B)), [np.arange(max(L - 1, 0)) for L in lens],
                 [max(L - 1, 0) for L in lens])
@@ -324,7 +324,7 @@ def test_multi_query_decode(fmt, nq, H):
     lens = np.array([1, 3, 8, 9, 64, 65, 133, 140, 300, 1000])
     d = synth.small(fmt=fmt, batch=len(lens), heads=H, lens=lens, seed=51 + nq, queries=nq)
     say("multi_query", fmt, nq, H, lens.tolist())
-    c = GpuCache(d)
+    c = GpuCache(d, seq_slots=np.random.default_rng(nq).permutation(d.B))
     c.fill()
     for ns in (0, 1, 3):
         out, lse = c.decode_mq(num_splits=ns)
