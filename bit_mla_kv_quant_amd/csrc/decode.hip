@@ -33,30 +33,41 @@ __device__ __forceinline__ void combine_term(const f32x4& ml, const f32x4& ov, f
   }
 }
 
-// Up to N splits with every partial in flight at once, then one pass.
+// Splits j0 .. j0+N-1 (those below ns) with every partial in flight at once,
+// merged into the running (M, sums): the running state is rescaled when this
+// round raises the maximum.
 template <int N>
-__device__ __forceinline__ void combine_all(const DecodeArgs& a, int64_t base, int ns, int d0,
-                                            float& M, f32x4& accv, float& ssum, float& fsum) {
+__device__ __forceinline__ void combine_round(const DecodeArgs& a, int64_t base, int j0, int ns,
+                                              int d0, float& M, f32x4& accv, float& ssum,
+                                              float& fsum) {
   f32x4 ml[N], ov[N];
 #pragma unroll
   for (int u = 0; u < N; ++u) {
-    if (u < ns) {
-      const int64_t e = base + (int64_t)u * a.H;
+    if (j0 + u < ns) {
+      const int64_t e = base + (int64_t)(j0 + u) * a.H;
       ml[u] = *(const f32x4*)(a.ws_ml + e * 4);
       ov[u] = *(const f32x4*)(a.ws_o + e * DC + d0);
     }
   }
+  float Mr = M;
 #pragma unroll
   for (int u = 0; u < N; ++u)
-    if (u < ns) M = fmaxf(M, ml[u][0]);
+    if (j0 + u < ns) Mr = fmaxf(Mr, ml[u][0]);
+  if (M != -INFINITY && Mr > M) {
+    const float r = __builtin_amdgcn_exp2f(M - Mr);
+    accv *= r;
+    ssum *= r;
+    fsum *= r;
+  }
+  M = Mr;
 #pragma unroll
   for (int u = 0; u < N; ++u)
-    if (u < ns) combine_term(ml[u], ov[u], M, accv, ssum, fsum);
+    if (j0 + u < ns) combine_term(ml[u], ov[u], M, accv, ssum, fsum);
 }
 
-// NMAX: 8 or 16 for plans of at most that many splits (all loads in flight
-// at once; separate instantiations keep the register count of the common
-// 8-split case low), 0 for longer plans (four splits at a time).
+// NMAX = 8 or 16: plans of at most that many splits, every partial in
+// flight at once (one round); NMAX = 0: longer plans, rounds of 16.
+// Separate instantiations keep the register count of the short plans low.
 template <int NMAX>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int b = blockIdx.z, H = a.H;
@@ -69,26 +80,9 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   f32x4 accv = {0.f, 0.f, 0.f, 0.f};
   float ssum = 0.f, fsum = 0.f, M = -INFINITY;
   if constexpr (NMAX > 0) {
-    combine_all<NMAX>(a, base, ns, d0, M, accv, ssum, fsum);
+    combine_round<NMAX>(a, base, 0, ns, d0, M, accv, ssum, fsum);       // ns <= NMAX
   } else {
-    for (int jj = 0; jj < ns; ++jj) M = fmaxf(M, a.ws_ml[(base + (int64_t)jj * H) * 4]);
-    int jj = 0;
-    for (; jj + 4 <= ns; jj += 4) {
-      f32x4 ml[4], ov[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t e = base + (int64_t)(jj + u) * H;
-        ml[u] = *(const f32x4*)(a.ws_ml + e * 4);
-        ov[u] = *(const f32x4*)(a.ws_o + e * DC + d0);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) combine_term(ml[u], ov[u], M, accv, ssum, fsum);
-    }
-    for (; jj < ns; ++jj) {
-      const int64_t e = base + (int64_t)jj * H;
-      combine_term(*(const f32x4*)(a.ws_ml + e * 4), *(const f32x4*)(a.ws_o + e * DC + d0), M,
-                   accv, ssum, fsum);
-    }
+    for (int j0 = 0; j0 < ns; j0 += 16) combine_round<16>(a, base, j0, ns, d0, M, accv, ssum, fsum);
   }
   if (M == -INFINITY) {                              // empty sequence
     *(f32x4*)o = f32x4{0.f, 0.f, 0.f, 0.f};
