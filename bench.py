@@ -100,6 +100,16 @@ def stored_traffic(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cache_accounting(ops, fmt, lens):
+    """Persistent cache bytes of the batch in the library's layout against a
+    BF16 paged cache: per sequence, its pages (plus an 8-byte reverse page
+    map each) and one protection buffer, against 64 x 1152 bytes per page."""
+    pb, prot = ops.mla_lb_page_bytes(fmt), ops.mla_lb_prot_bytes_per_seq()
+    packed = sum(-(-L // PAGE) * (pb + 8) + prot for L in lens)
+    bf16 = sum(-(-L // PAGE) * PAGE * ROW_BYTES for L in lens)
+    return {"packed": packed, "bf16": bf16, "ratio": round(bf16 / packed, 4)}
+
+
 # --------------------------------------------------------------- workload ---
 def upload(ops, torch, d, fmt, dev):
     """Page pool + protection buffers filled through kv_quant_append with the
@@ -392,6 +402,7 @@ def main():
         "decode_kv_tokens_per_s": round(kv_tokens / (dec_ms * 1e-3), 1),
         "append_ms": round(app_ms, 5),
         "packed_bytes_per_token": TOKEN_BYTES[fmt], "bf16_bytes_per_token": ROW_BYTES,
+        "cache_bytes": cache_accounting(ops, fmt, lens),
     }
     if not args.no_cpu:
         log("cpu oracle leg")
