@@ -12,7 +12,7 @@ import pytest
 from bit_mla_kv_quant_amd import synth
 from oracle import attention, layout, quant
 
-from gpu_helpers import GpuCache, oracle_decode, oracle_decode_mq, oracle_page, rel_l2
+from gpu_helpers import GpuCache, oracle_decode, oracle_decode_mq, oracle_page, rel_l2, t_bf16, t_i32
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -454,3 +454,44 @@ def test_calibrated_scales_through_kernels():
         e_sc = transforms.nmse(o_sc[b] / s_c, ref)
         say(f"  seq {b}: NMSE plain {e_rtn:.2e}, scaled {e_sc:.2e}")
         assert e_sc < e_rtn / 3, (e_rtn, e_sc)
+
+
+# ------------------------------------------------------------ host guards ---
+@pytest.mark.parametrize("H", [16, 128])
+def test_seq_lens_clamped_to_max_seq_len(H):
+    """seq_lens beyond max_seq_len are clamped on the device: a sequence whose
+    cache holds 700 tokens, passed as 1000 with max_seq_len 700, decodes
+    exactly its 700 tokens."""
+    d = synth.small(fmt="C4R4", batch=2, heads=H, lens=(300, 700), seed=71, extra_tokens=300)
+    say("clamp", H)
+    c = GpuCache(d)
+    c.fill()
+    out, lse = c.decode(lens=[300, 1000], max_seq_len=700)
+    check_decode(d, c, out, lse, [300, 700])
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_unusable_block_table_entries_are_skipped(H):
+    """Block-table entries outside [0, num_pages) are never dereferenced:
+    the call completes, its outputs are finite, and the other sequences'
+    results are bit-identical to the run with a valid table."""
+    from bit_mla_kv_quant_amd import ops
+    d = synth.small(fmt="C4R4", batch=3, heads=H, lens=(900, 640, 1200), seed=72)
+    say("unusable pages", H)
+    c = GpuCache(d)
+    c.fill()
+    ref_out, ref_lse = c.decode()
+    bt = d.block_table.copy()
+    bt[1, 3] = -1
+    bt[1, 7] = d.num_pages + 5
+    for ns in (0, 1):
+        out, lse = ops.mla_decode_lowbit(
+            "C4R4", t_bf16(d.q_lat), t_bf16(d.q_rope), c.pages, c.prot, c.seq_slot,
+            t_i32(bt), t_i32(d.lens), int(d.lens.max()), d.scale, num_splits=ns)
+        torch.cuda.synchronize()
+        out = out.cpu().numpy().astype(np.float64)
+        lse = lse.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(out[1])) and np.all(np.isfinite(lse[1]))
+        if ns == 0:
+            np.testing.assert_array_equal(out[[0, 2]], ref_out[[0, 2]])
+            np.testing.assert_array_equal(lse[[0, 2]], ref_lse[[0, 2]])
