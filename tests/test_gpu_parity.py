@@ -76,7 +76,7 @@ def test_dequant_dump_bit_exact(fmt):
         np.testing.assert_array_equal(got, want, err_msg=f"page {pid}")
 
 
-@pytest.mark.parametrize("fmt", ["C4R4", "C4R4F"])
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "C4R4F"])
 def test_dequant_edge_values(fmt):
     """Constant groups, tiny (subnormal-scale) ranges and huge ranges survive
     the GPU writer and reconstruction bit for bit."""
@@ -392,6 +392,26 @@ def test_config2_c2r4_long():
 
 def test_config3_v2_h128():
     _full_config(3, sample_b=[0, 15])
+
+
+def test_config2_fused_step():
+    """The long-context C2R4 workload as the bench runs it: every sequence
+    holds its first L-1 tokens, and one fused call stores token L-1 and
+    decodes; sampled sequences against the oracle, the written pages
+    byte-identical to the oracle's."""
+    wl = synth.WORKLOADS[2]
+    say("config 2 fused", wl.name, "drawing")
+    d = synth.draw(wl)
+    c = GpuCache(d)
+    lens = d.lens.astype(np.int64)
+    c.append(list(range(d.B)), [np.arange(L - 1) for L in lens], [L - 1 for L in lens])
+    out, lse = c.fused_step(lens)
+    w = check_decode(d, c, out, lse, lens, which=[0, 31, 63])
+    say("config 2 fused worst rel-L2 on sampled sequences", f"{w:.2e}")
+    pages = c.pages.cpu().numpy()
+    for b in (0, 63):
+        pid = d.block_table[b, (lens[b] - 1) // 64]
+        np.testing.assert_array_equal(pages[pid], oracle_page(d, pid, lens))
 
 
 def test_config5_v2lite_fp32_rope_metadata():
