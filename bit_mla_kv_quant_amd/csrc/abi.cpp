@@ -235,8 +235,9 @@ int mla_lb_channel_stat(const uint16_t* x, int64_t rows, int32_t n, double pct, 
       col[static_cast<size_t>(r)] = std::fabs(static_cast<double>(f));
     }
     std::sort(col.begin(), col.end());
-    const double v = col[static_cast<size_t>(lo)] +
-                     (col[static_cast<size_t>(hi)] - col[static_cast<size_t>(lo)]) * frac;
+    // interpolate from the nearer end (the form numpy's percentile uses)
+    const double va = col[static_cast<size_t>(lo)], vb = col[static_cast<size_t>(hi)];
+    const double v = frac < 0.5 ? va + (vb - va) * frac : vb - (vb - va) * (1.0 - frac);
     stat[j] = static_cast<float>(v);
   }
   return MLA_LB_OK;
