@@ -191,3 +191,36 @@ def test_calibration_helpers_match_oracle(ops):
     assert lib.mla_lb_channel_stat(FAKE, 0, 4, 99.9, FAKE) == -2
     assert lib.mla_lb_channel_stat(FAKE, 4, 4, 101.0, FAKE) == -2
     assert lib.mla_lb_channel_stat(None, 4, 4, 99.9, FAKE) == -1
+
+
+def test_header_is_plain_c_and_links(ops, tmp_path):
+    """A C99 caller (gcc -pedantic) compiles against include/mla_lowbit.h,
+    links libmla_lowbit.so and gets the host queries' answers."""
+    import shutil
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    src = tmp_path / "caller.c"
+    src.write_text(r'''
+#include <string.h>
+#include "mla_lowbit.h"
+int main(void) {
+  float stat[4] = {4.0f, 1.0f, 0.25f, 16.0f}, s[4];
+  size_t ws = 0;
+  if (mla_lb_page_bytes(MLA_LB_C4R4) != 20736 || mla_lb_page_bytes(MLA_LB_C2R4) != 12544) return 1;
+  if (mla_lb_prot_bytes_per_seq() != 152064) return 2;
+  if (strlen(mla_lb_strerror(MLA_LB_EWORKSPACE)) == 0) return 3;
+  if (mla_decode_lowbit_workspace(MLA_LB_C4R4, 2, 16, 200, 2, &ws) != MLA_LB_OK) return 4;
+  if (ws != (size_t)2 * 2 * 16 * 516 * 4) return 5;
+  if (mla_lb_smooth_scales(stat, 4, 1.0f, 1, s) != MLA_LB_OK) return 6;
+  if (s[0] != 0.25f || s[1] != 0.25f || s[2] != 0.0625f || s[3] != 0.0625f) return 7;
+  if (mla_decode_lowbit(MLA_LB_C4R4, 0, 0, 0, 1, 0, 1, 0, 0, 1, 0, 64, 1, 16, 0.1f, 0, 0, 0,
+                        0, 0, 0) != MLA_LB_EINVAL) return 8;
+  return 0;
+}
+''')
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(ops.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), str(src), "-L", libdir, "-lmla_lowbit",
+                    f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    assert subprocess.run([str(exe)]).returncode == 0
