@@ -336,6 +336,34 @@ def test_multi_query_decode(fmt, nq, H):
             np.testing.assert_array_equal(lse[:, 0], l1)
 
 
+@pytest.mark.parametrize("nq", [2, 8])
+def test_multi_query_score_jumps(nq):
+    """Score jumps with several queries: a token far above everything before
+    it for one query row, planted where some rows' causal prefixes end before
+    it (the last token) or include it (a packed token); the running reference
+    of each row moves independently."""
+    H = 16
+    d = synth.small(fmt="C4R4", batch=2, heads=H, lens=(1500, 900), seed=33, queries=nq)
+    l2e = 1.4426950408889634
+
+    def plant(b, pos, row, log2_score):
+        q = quant.bf16_to_f32(d.q_lat[b, row]).astype(np.float64)
+        alpha = log2_score / (np.linalg.norm(q) ** 2 * d.scale * l2e)
+        d.c[b][pos] = quant.f32_to_bf16((alpha * q).astype(np.float32))
+        d.kr[b][pos] = 0
+
+    plant(0, 400, 0, 100.0)                 # packed; query 0, head 0
+    plant(0, 1499, (nq - 1) * H + 3, 150.0)  # the last token: only the last query sees it
+    plant(1, 850, H + 5, 120.0)              # protected window row; query 1, head 5
+    say("multi_query_score_jumps", nq)
+    c = GpuCache(d)
+    c.fill()
+    for ns in (1, 0, 5):
+        out, lse = c.decode_mq(num_splits=ns)
+        w = check_decode_mq(d, out, lse, d.lens)
+        say("  num_splits", ns, "worst rel-L2", f"{w:.2e}")
+
+
 def test_config6_multi_query_v2lite():
     wl = synth.WORKLOADS[6]
     say("config 6", wl.name, "drawing")
