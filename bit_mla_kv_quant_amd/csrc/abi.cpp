@@ -25,7 +25,7 @@ static size_t page_bytes_of(int f) {
 // pps pages.  Automatic choice: enough (split, sequence, head-block)
 // workgroups to keep every CU busy, but no split shorter than a minimum
 // number of pages (each split costs a heads x 512 fp32 partial write).  Head
-// blocks are 128 heads when H is a multiple of 128, else 16.
+// blocks are 128 rows when use_rows128(H), else 16.
 
 Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits) {
   Plan p{1, 1, 0};
@@ -35,8 +35,8 @@ Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits) {
   if (num_splits > 0) {
     ns = num_splits;
   } else {
-    const bool h128 = H % 128 == 0;
-    const int64_t groups = static_cast<int64_t>(B) * (h128 ? H / 128 : H / 16);
+    const bool h128 = mlb::use_rows128(H);
+    const int64_t groups = static_cast<int64_t>(B) * (h128 ? (H + 127) / 128 : H / 16);
     ns = (static_cast<int64_t>(kNumCUs) * kWavesTarget + groups - 1) / groups;
     const int64_t cap = P / (h128 ? kMinPagesPerSplit128 : kMinPagesPerSplit);
     if (ns > cap) ns = cap;

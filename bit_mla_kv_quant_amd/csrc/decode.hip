@@ -112,7 +112,7 @@ __global__ __launch_bounds__(512) void dequant_dump_kernel(const uint8_t* pages,
 }
 
 int launch_decode(int f, const DecodeArgs& a, hipStream_t stream) {
-  if (a.H % 128 == 0) {
+  if (use_rows128(a.H)) {
     // 128-head blocks: one reconstruction of each page serves all heads
     if (launch_decode128(f, a, stream) != 0) return -5;
   } else {

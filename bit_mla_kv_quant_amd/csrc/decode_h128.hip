@@ -75,6 +75,10 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
   const int l32 = lane & 31, h = lane >> 5;        // attention role
   const int H = a.H;
   const int head = HB * hb + 32 * wave + l32;      // this lane's head
+  // a padding row (past H) repeats row 0 of the sequence, query and causal
+  // length both, and writes nothing
+  const bool live = head < H;
+  const int qrow = live ? head : 0;
 
   int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
@@ -84,13 +88,14 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
   const int p0 = j * a.pps;
   const int p1 = min(p0 + a.pps, npages);
   const bool single = a.nsplit == 1;
+  const int rows_here = min(HB, H - HB * hb);      // rows past H are padding
   if (p0 >= p1) {
     if (single && j == 0) {                        // empty sequence: out 0, lse -inf
       float* o = a.out + ((int64_t)b * H + HB * hb) * DC;
-      for (int idx = threadIdx.x; idx < HB * DC / 4; idx += 256)
+      for (int idx = threadIdx.x; idx < rows_here * DC / 4; idx += 256)
         *(f32x4*)(o + 4 * idx) = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (threadIdx.x < HB) a.lse[(int64_t)b * H + HB * hb + threadIdx.x] = -INFINITY;
-    } else if (!single && threadIdx.x < HB) {      // no tokens: m = -inf for the merge
+      if (threadIdx.x < rows_here) a.lse[(int64_t)b * H + HB * hb + threadIdx.x] = -INFINITY;
+    } else if (!single && threadIdx.x < rows_here) {   // no tokens: m = -inf for the merge
       const int64_t base = ((int64_t)b * a.nsplit + j) * H + HB * hb + threadIdx.x;
       *(f32x4*)(a.ws_ml + base * 4) = f32x4{-INFINITY, 0.f, 0.f, 0.f};
     }
@@ -99,7 +104,7 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
   const int np = p1 - p0;
   // tokens the lane's row attends to: the causal prefix of its query, all L
   // when there is one query per sequence
-  const int L_row = L - (a.nq - 1 - head / a.hq);
+  const int L_row = L - (a.nq - 1 - qrow / a.hq);
   const bool fused = a.new_c != nullptr;
   // fused writer: the middle split of the sequence (first head block)
   // stores the newest token before its page loop.  No workgroup of this
@@ -126,10 +131,10 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
   // content dims 16s + 8h .. +7, slices 32..35 the RoPE dims 16(s-32) + 8h.
   bf16x8 qv[36];
   {
-    const uint16_t* ql = a.q_lat + ((int64_t)b * H + head) * DC + 8 * h;
+    const uint16_t* ql = a.q_lat + ((int64_t)b * H + qrow) * DC + 8 * h;
 #pragma unroll
     for (int s = 0; s < 32; ++s) qv[s] = *(const bf16x8*)(ql + 16 * s);
-    const uint16_t* qr = a.q_rope + ((int64_t)b * H + head) * DR + 8 * h;
+    const uint16_t* qr = a.q_rope + ((int64_t)b * H + qrow) * DR + 8 * h;
 #pragma unroll
     for (int s = 0; s < 4; ++s) qv[32 + s] = *(const bf16x8*)(qr + 16 * s);
   }
@@ -324,6 +329,7 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
 
   // ---- outputs: the weight sum of the head over its two lanes
   const float f_tot = f_run + __shfl_xor(f_run, 32, 64);
+  if (!live) return;
   if (single) {
     const float inv = f_tot > 0.f ? 1.0f / f_tot : 0.f;
     float* o = a.out + ((int64_t)b * H + head) * DC + 4 * h;
@@ -350,7 +356,7 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
 }
 
 int launch_decode128(int f, const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.nsplit, a.B, a.H / HB), block(256);
+  const dim3 grid(a.nsplit, a.B, (a.H + HB - 1) / HB), block(256);
   if (f == 0)
     hipLaunchKernelGGL(decode128_kernel<0>, grid, block, 0, stream, a);
   else if (f == 1)

@@ -52,6 +52,18 @@ struct DecodeArgs {
   uint16_t* wprot;        // == prot
 };
 
+// Which decode kernel serves `rows` query rows per sequence (a multiple of
+// 16): the 16-row kernel reconstructs each page once per 16 rows, the 128-row
+// kernel once per block of up to 128 rows (rows past the last multiple of 128
+// are padding it masks).  Measured on MI355X at batch 32 x 8192 C4R4 tokens, a
+// 128-row block costs about as much as five 16-row groups (64 rows: 0.109 ms
+// with 16-row groups, 0.149 ms padded; 96 rows: 0.187 vs 0.155 ms), so the
+// 128-row kernel is taken when 5 * ceil(rows / 128) < ceil(rows / 16).
+inline bool use_rows128(int32_t rows) {
+  const int64_t r = rows;
+  return 5 * ((r + 127) / 128) < (r + 15) / 16;
+}
+
 // Split plan: how a max_seq_len sequence is cut into splits.
 struct Plan {
   int32_t pps;       // pages per split (>= 1)

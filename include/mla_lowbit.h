@@ -244,8 +244,9 @@ int mla_decode_lowbit_mq_workspace(int f, int32_t B, int32_t nq, int32_t H,
  * with (c~_i, k~_R,i) read as in mla_decode_lowbit for a sequence of length
  * L: the protected set is that of L [QuantMLA §3.3, App. C.5] for every
  * query of the call (the cache holds no other state).  nq = 1 is exactly
- * mla_decode_lowbit.  The nq*H query rows share each reconstructed page; when
- * nq*H is a multiple of 128 the 128-row matrix-core kernel runs.
+ * mla_decode_lowbit.  The nq*H query rows share each reconstructed page: 96,
+ * 112, 128 rows and from 176 up run on the 128-row matrix-core kernel (the
+ * last block padded), the other counts on 16-row groups.
  *
  *   q_lat  [B][nq][H][512] bf16,  q_rope [B][nq][H][64] bf16
  *   nq >= 1 with nq*H <= MLA_LB_MAX_ROWS; H as in mla_decode_lowbit

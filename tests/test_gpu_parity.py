@@ -145,7 +145,7 @@ EDGE_LENS = (0, 1, 3, 4, 5, 63, 64, 65, 127, 128, 129, 131, 132, 133, 200, 1000)
 
 
 @pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "C4R4F"])
-@pytest.mark.parametrize("H", [16, 32, 128])
+@pytest.mark.parametrize("H", [16, 32, 64, 96, 128])
 def test_decode_edge_lengths(fmt, H):
     d = synth.small(fmt=fmt, batch=len(EDGE_LENS), heads=H, lens=EDGE_LENS, seed=H)
     say("decode_edge", fmt, H)
@@ -249,7 +249,7 @@ def test_token_aging(fmt):
 
 # ---------------------------------------------------- fused writer + decode ---
 @pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "C4R4F"])
-@pytest.mark.parametrize("H", [16, 32, 128])
+@pytest.mark.parametrize("H", [16, 64, 96, 128])
 def test_fused_step_equals_append_then_decode(fmt, H):
     """mla_decode_lowbit_append writes the same page bytes and protection
     rows as kv_quant_append of each sequence's newest token, and returns the
@@ -315,12 +315,14 @@ def check_decode_mq(d, out, lse, lens, which=None, fmt=None):
 
 
 @pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "C4R4F"])
-@pytest.mark.parametrize("nq,H", [(1, 16), (2, 16), (3, 32), (8, 16), (2, 128)])
+@pytest.mark.parametrize("nq,H", [(1, 16), (2, 16), (3, 32), (4, 16), (2, 48), (3, 48), (8, 16), (2, 128)])
 def test_multi_query_decode(fmt, nq, H):
     """nq queries per sequence, each over its causal prefix, against the
     oracle; lengths below nq (empty prefixes), at sink / page / window edges
-    and over several splits.  8 x 16 and 2 x 128 rows take the 128-row
-    kernel, the others the 16-row one; nq = 1 must equal mla_decode_lowbit."""
+    and over several splits.  Up to 80 rows and 144 rows take the 16-row
+    kernel; 96 and 128 rows take the 128-row one, 2 x 48 = 96 rows padded to
+    128 with a query boundary inside the block; nq = 1 must equal
+    mla_decode_lowbit."""
     lens = np.array([1, 3, 8, 9, 64, 65, 133, 140, 300, 1000])
     d = synth.small(fmt=fmt, batch=len(lens), heads=H, lens=lens, seed=51 + nq, queries=nq)
     say("multi_query", fmt, nq, H, lens.tolist())
