@@ -338,6 +338,42 @@ def test_multi_query_decode(fmt, nq, H):
             np.testing.assert_array_equal(lse[:, 0], l1)
 
 
+@pytest.mark.parametrize("nq,H", [(8, 128), (64, 16)])
+def test_multi_query_max_rows(nq, H):
+    """The largest call: nq * H = 1024 query rows per sequence (eight
+    128-row blocks), ragged lengths around the window edges, against the
+    oracle for every row, single-split and split."""
+    assert nq * H == 1024                          # MLA_LB_MAX_ROWS
+    lens = np.array([70, 133, 600])
+    d = synth.small(fmt="C4R4", batch=len(lens), heads=H, lens=lens, seed=82, queries=nq)
+    say("max rows", nq, H, lens.tolist())
+    c = GpuCache(d)
+    c.fill()
+    for ns in (0, 1):
+        out, lse = c.decode_mq(num_splits=ns)
+        w = check_decode_mq(d, out, lse, lens)
+        say("  num_splits", ns, "worst rel-L2", f"{w:.2e}")
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_many_sequences(H):
+    """1024 sequences of 0-199 tokens in one call (grid of 1024 sequences,
+    shuffled cache slots): 48 sampled sequences, the empty one and those at
+    the window edges among them, against the oracle."""
+    rng = np.random.default_rng(83)
+    lens = rng.integers(1, 200, size=1024)
+    lens[:5] = [0, 1, 4, 132, 133]
+    d = synth.small(fmt="C4R4", batch=len(lens), heads=H, lens=lens, seed=83 + H)
+    say("many sequences", H, len(lens))
+    c = GpuCache(d, seq_slots=rng.permutation(d.B))
+    c.fill()
+    which = sorted(set(range(5)) | set(rng.choice(len(lens), 43, replace=False).tolist()))
+    for ns in (0, 1):
+        out, lse = c.decode(num_splits=ns)
+        w = check_decode(d, c, out, lse, lens, which=which)
+        say("  num_splits", ns, "worst rel-L2", f"{w:.2e}")
+
+
 @pytest.mark.parametrize("nq", [2, 8])
 def test_multi_query_score_jumps(nq):
     """Score jumps with several queries: a token far above everything before
