@@ -47,6 +47,8 @@ Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits) {
   ns = (P + pps - 1) / pps;
   p.pps = static_cast<int32_t>(pps);
   p.nsplit = static_cast<int32_t>(ns);
+  // B x nsplit x rows x (512 + 4) fp32: within the entry points' bounds
+  // (B <= 65535, nsplit <= 2^25 pages, rows <= 1024) below 2^63
   if (ns > 1)
     p.ws_bytes = static_cast<size_t>(B) * static_cast<size_t>(ns) * static_cast<size_t>(H) *
                  (512 + 4) * sizeof(float);
@@ -98,6 +100,7 @@ int mla_decode_lowbit_workspace(int f, int32_t B, int32_t H, int32_t max_seq_len
   if (B < 1 || H < 16 || H > MLA_LB_MAX_HEADS || H % 16 != 0 || max_seq_len < 0 ||
       num_splits < 0)
     return MLA_LB_ESHAPE;
+  if (B > 65535) return MLA_LB_ESHAPE;               // as the decode call
   *bytes = mlb::make_plan(B, H, max_seq_len, num_splits).ws_bytes;
   return MLA_LB_OK;
 }
@@ -201,6 +204,7 @@ int mla_decode_lowbit_mq_workspace(int f, int32_t B, int32_t nq, int32_t H,
   if (B < 1 || H < 16 || H > MLA_LB_MAX_HEADS || H % 16 != 0 || nq < 1 ||
       static_cast<int64_t>(nq) * H > MLA_LB_MAX_ROWS || max_seq_len < 0 || num_splits < 0)
     return MLA_LB_ESHAPE;
+  if (B > 65535) return MLA_LB_ESHAPE;               // as the decode call
   *bytes = mlb::make_plan(B, nq * H, max_seq_len, num_splits).ws_bytes;
   return MLA_LB_OK;
 }

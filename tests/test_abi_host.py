@@ -167,6 +167,15 @@ def test_workspace_plan(ops):
         assert n % (B * H * 516 * 4) == 0
     with pytest.raises(ops.MlaLowbitError):
         ops.mla_decode_lowbit_workspace("C4R4", 1, 20, 100, 0)
+    # the largest plan the entry points accept (65535 sequences, 2^25 one-page
+    # splits, 1024 query rows) is sized exactly, below 2^63
+    big = 2**31 - 1
+    n = ops.mla_decode_lowbit_mq_workspace("C4R4", 65535, 8, 128, big, big)
+    assert n == 65535 * 2**25 * 1024 * 516 * 4 and n < 2**63
+    for call in (lambda: ops.mla_decode_lowbit_workspace("C4R4", 65536, 16, 1000, 0),
+                 lambda: ops.mla_decode_lowbit_mq_workspace("C4R4", 65536, 2, 16, 1000, 0)):
+        with pytest.raises(ops.MlaLowbitError):      # B beyond the grid limit
+            call()
 
 
 def test_calibration_helpers_match_oracle(ops):
