@@ -367,7 +367,9 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
 
   // ---- merge the eight waves through LDS (log-sum-exp rule).  The
   // accumulators are only stored, RD output dims per round; thread t merges
-  // head t/32, dims 8(t%32) .. +7 of the round.
+  // head t/32, dims 4(t%32) .. +3 and RD/2 + 4(t%32) .. +3 of the round, so
+  // the 32 threads of a head read contiguous 16-byte pieces (no two lanes of
+  // a read on one bank).
   float f_tot = f_run + __shfl_xor(f_run, 16, 64);
   f_tot += __shfl_xor(f_tot, 32, 64);              // lane n16: head n16's sum over the wave
   constexpr int RD = 256;                                // output dims per round
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
     mm[(wave * 16 + n16) * 2 + 1] = f_tot;
   }
   __syncthreads();
-  const int hh = threadIdx.x >> 5, d8 = 8 * (threadIdx.x & 31);
+  const int hh = threadIdx.x >> 5, d4 = 4 * (threadIdx.x & 31);
   const int head = 16 * hg + hh;
   float M = -INFINITY;
 #pragma unroll
@@ -415,11 +417,11 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
     f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      o0 += wt[w] * *(const f32x4*)(mo + (w * 16 + hh) * MP + d8);
-      o1 += wt[w] * *(const f32x4*)(mo + (w * 16 + hh) * MP + d8 + 4);
+      o0 += wt[w] * *(const f32x4*)(mo + (w * 16 + hh) * MP + d4);
+      o1 += wt[w] * *(const f32x4*)(mo + (w * 16 + hh) * MP + RD / 2 + d4);
     }
-    *(f32x4*)(dst + RD * r + d8) = o0 * osc;
-    *(f32x4*)(dst + RD * r + d8 + 4) = o1 * osc;
+    *(f32x4*)(dst + RD * r + d4) = o0 * osc;
+    *(f32x4*)(dst + RD * r + RD / 2 + d4) = o1 * osc;
     __syncthreads();
   }
   if (writer) fused_store<F>(a, fresh_row, b, L, sq, wave, NW, lane);
