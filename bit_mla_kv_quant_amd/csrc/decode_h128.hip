@@ -7,7 +7,9 @@
 // by all heads from LDS.  decode128_kernel<F>: one 256-thread workgroup
 // (4 waves, one per SIMD) per (split j, sequence b, 128-head block), walking
 // the split's pages through two LDS tiles [64 tokens][576 dims] of
-// reconstructed bf16.  In step k every wave does two jobs:
+// reconstructed bf16.  A call whose query rows are not a multiple of 128
+// pads its last block: rows past H repeat row 0 of the sequence and write
+// nothing.  In step k every wave does two jobs:
 //   reconstruct page k+1 -- wave w takes token slots 16w .. 16w+15; lane
 //      (n16, g) owns slot 16w + n16 and, in it, content groups 2g and 2g+1
 //      (dims 128g .. 128g+127) and RoPE dims 16g .. 16g+15, from packed codes
