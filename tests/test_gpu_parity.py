@@ -542,6 +542,66 @@ def test_calibrated_scales_through_kernels():
         assert e_sc < e_rtn / 3, (e_rtn, e_sc)
 
 
+# ------------------------------------------------------------ HIP graphs ---
+@pytest.mark.parametrize("H", [16, 128])
+def test_graph_replay_matches_eager(H):
+    """The split decode (workspace and combine inside the graph) and the fused
+    step captured in HIP graphs, the launch mode the benchmark times: six
+    replays each, with eager calls on the same workspace, buffer fills and
+    host synchronisations between them, every replay bit-identical to the
+    eager call (outputs, and for the fused step the page bytes and
+    protection rows)."""
+    from bit_mla_kv_quant_amd import ops
+    lens = np.array([700, 1000, 133, 5])
+    d = synth.small(fmt="C4R4", batch=len(lens), heads=H, lens=lens, seed=91)
+    say("graph replay", H)
+    c = GpuCache(d)
+    c.fill()
+    ql, qr, tl = t_bf16(d.q_lat), t_bf16(d.q_rope), t_i32(lens)
+    lat = t_bf16(np.stack([d.c[b][L - 1] for b, L in enumerate(lens)]))
+    kr = t_bf16(np.stack([d.kr[b][L - 1] for b, L in enumerate(lens)]))
+    msl, ns = int(lens.max()), 3
+    ws = torch.empty(ops.mla_decode_lowbit_workspace("C4R4", d.B, H, msl, ns),
+                     dtype=torch.uint8, device=c.pages.device)
+    out = torch.empty((d.B, H, 512), dtype=torch.float32, device=c.pages.device)
+    lse = torch.empty((d.B, H), dtype=torch.float32, device=c.pages.device)
+    stream = torch.cuda.Stream()
+
+    def decode():
+        ops.mla_decode_lowbit("C4R4", ql, qr, c.pages, c.prot, c.seq_slot, c.block_table, tl,
+                              msl, d.scale, ns, workspace=ws, out=out, lse=lse, stream=stream)
+
+    def fused():
+        ops.mla_decode_lowbit_append("C4R4", lat, kr, ql, qr, c.pages, c.prot, c.seq_slot,
+                                     c.block_table, tl, msl, d.scale, ns, workspace=ws,
+                                     out=out, lse=lse, stream=stream)
+
+    for step in (decode, fused):
+        with torch.cuda.stream(stream):
+            step()
+        stream.synchronize()
+        ref_o, ref_l = out.cpu().clone(), lse.cpu().clone()
+        ref_p, ref_r = c.pages.cpu().clone(), c.prot.cpu().clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step()
+        for rep in range(6):
+            with torch.cuda.stream(stream):
+                out.fill_(float("nan"))
+                lse.fill_(float("nan"))
+                if rep % 2:                        # an eager call on the same workspace
+                    ops.mla_decode_lowbit("C4R4", ql, qr, c.pages, c.prot, c.seq_slot,
+                                          c.block_table, tl, msl, d.scale, 2, workspace=ws,
+                                          out=out, lse=lse, stream=stream)
+            stream.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.cpu(), ref_o) and torch.equal(lse.cpu(), ref_l), (step, rep)
+            assert torch.equal(c.pages.cpu(), ref_p) and torch.equal(c.prot.cpu(), ref_r), (step, rep)
+        say("  ", step.__name__, "6 replays bit-identical")
+    check_decode(d, c, ref_o.numpy().astype(np.float64), ref_l.numpy().astype(np.float64), lens)
+
+
 # ------------------------------------------------------------ host guards ---
 @pytest.mark.parametrize("H", [16, 128])
 def test_seq_lens_clamped_to_max_seq_len(H):
