@@ -49,7 +49,7 @@ TOKEN_BYTES = {"C4R4": 324, "C2R4": 196, "C4R4F": 328}   # packed codes + (scale
 KERNEL_SOURCES = ("bit_mla_kv_quant_amd/csrc/decode.hip", "bit_mla_kv_quant_amd/csrc/decode_h16.hip",
                   "bit_mla_kv_quant_amd/csrc/decode_h128.hip", "bit_mla_kv_quant_amd/csrc/dequant.h",
                   "bit_mla_kv_quant_amd/csrc/common.h", "bit_mla_kv_quant_amd/csrc/quantize.h",
-                  "bit_mla_kv_quant_amd/csrc/internal.h")
+                  "bit_mla_kv_quant_amd/csrc/internal.h", "bit_mla_kv_quant_amd/build.py")
 
 
 def log(*a):
