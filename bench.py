@@ -8,8 +8,10 @@ window refresh), then decode over every cached token (paged low-bit + BF16
 protected rows, one global softmax, split-KV merge).  By default both run in
 one launch (mla_decode_lowbit_append); --step separate times kv_quant_append
 followed by mla_decode_lowbit.
-The headline workload is the DeepSeek-V2-Lite-shaped C4R4 cache: batch 32,
-16 heads, 8192 tokens per sequence, 64-token pages with a shuffled block table.
+The default workload is the largest single-GPU one, the 128K cache-pressure
+C4R4 cache: batch 8, 128 heads sharing one latent (DeepSeek-V2 shape), 96K to
+128K tokens per sequence, 64-token pages with a shuffled block table, the
+writer of every sequence's newest token interleaved with each decode step.
 
 Inputs are synthetic and seeded (bit_mla_kv_quant_amd.synth), uploaded before
 timing.  To keep the 256 MB last-level cache from serving the KV history, the
@@ -180,39 +182,85 @@ def footprint(r):
 
 
 # ------------------------------------------------------------ cpu leg ------
-def cpu_baseline(d, fmt, budget_s=12.0):
-    """The CPU oracle (as it stands) decoding whole sequences of the same
-    workload, cycling through the batch, until about budget_s seconds of work
-    are done (at least one sequence)."""
-    from oracle import attention
+def _cpu_model():
     try:
-        import threadpoolctl
-        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing: numpy's BLAS default
-        threads = len(os.sched_getaffinity(0))
-    tokens, nseq, t0 = 0, 0, time.perf_counter()
-    while True:
-        b = nseq % d.B
-        L = int(d.lens[b])
-        nq = d.wl.queries
-        if nq > 1:
-            attention.decode_multi(d.c[b][:L], d.kr[b][:L], d.q_lat[b].reshape(nq, d.H, 512),
-                                   d.q_rope[b].reshape(nq, d.H, 64), fmt, d.scale)
-        else:
-            attention.decode_sequence(d.c[b][:L], d.kr[b][:L], d.q_lat[b], d.q_rope[b], fmt,
-                                      d.scale)
-        tokens += L
-        nseq += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(tokens / dt, 1), "unit": "KV-tokens/s", "cores": int(threads),
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _oracle_leg(d, fmt, budget_s, threads):
+    """The CPU oracle (as it stands) decoding whole sequences of the workload,
+    cycling through the batch, with BLAS limited to `threads`, until about
+    budget_s seconds of work are done (at least one sequence).  The two
+    phases are timed apart: unpack + dequantize (the fp32 quantizer and
+    reconstruction of every token, oracle.attention.effective_rows) and fp64
+    attention (oracle.attention.attend / the causal form for several
+    queries)."""
+    import threadpoolctl
+    from oracle import attention, quant
+    t_deq = t_att = 0.0
+    tokens = nseq = 0
+    nq = d.wl.queries
+    with threadpoolctl.threadpool_limits(limits=threads, user_api="blas"):
+        used = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
+                    if i.get("user_api") == "blas"] or [1])
+        while True:
+            b = nseq % d.B
+            L = int(d.lens[b])
+            t0 = time.perf_counter()
+            rows = attention.effective_rows(d.c[b][:L], d.kr[b][:L], fmt)
+            t1 = time.perf_counter()
+            ql = quant.bf16_to_f32(d.q_lat[b]).astype(np.float64)
+            qr = quant.bf16_to_f32(d.q_rope[b]).astype(np.float64)
+            if nq > 1:
+                ql, qr = ql.reshape(nq, d.H, 512), qr.reshape(nq, d.H, 64)
+                for j in range(nq):
+                    n = L - nq + 1 + j
+                    if n > 0:
+                        attention.attend(ql[j], qr[j], rows[:n], d.scale)
+            else:
+                attention.attend(ql, qr, rows, d.scale)
+            t2 = time.perf_counter()
+            t_deq += t1 - t0
+            t_att += t2 - t1
+            tokens += L
+            nseq += 1
+            if t_deq + t_att >= budget_s:
+                break
+    return {"tokens": tokens, "sequences": nseq, "dequant_s": round(t_deq, 3),
+            "attention_s": round(t_att, 3), "blas_threads": int(used),
+            "kv_tokens_per_s": round(tokens / (t_deq + t_att), 1),
+            "dequant_kv_tokens_per_s": round(tokens / t_deq, 1),
+            "attention_kv_tokens_per_s": round(tokens / t_att, 1)}
+
+
+def cpu_baseline(d, fmt, budget_s=12.0, budget_1t_s=8.0):
+    """The oracle timed on the host: once with BLAS on every core of this
+    process's affinity set, once on one thread; phases reported apart."""
+    import threadpoolctl
+    aff = sorted(os.sched_getaffinity(0))
+    ncores = len(aff)
+    allc = _oracle_leg(d, fmt, budget_s, ncores)
+    one = _oracle_leg(d, fmt, budget_1t_s, 1)
+    blas = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+    blas_name = (f"{blas[0].get('internal_api')} {blas[0].get('version')}" if blas else "none")
+    return {"value": allc["kv_tokens_per_s"], "unit": "KV-tokens/s", "cores": allc["blas_threads"],
             "kind": "oracle",
-            "sample": f"{nseq} sequence decodes cycling over the {d.B} sequences of the same "
-                      f"workload ({tokens} KV tokens, {d.wl.queries} x {d.H} query rows): fp32 "
-                      f"quantize/dequant of "
-                      f"every token + fp64 attention, {dt:.1f} s on {threads} BLAS threads"}
+            "sample": (f"{allc['sequences']} whole-sequence decodes cycling over the {d.B} "
+                       f"sequences of the same workload ({allc['tokens']} KV tokens, "
+                       f"{d.wl.queries} x {d.H} query rows): fp32 quantize + dequantize of every "
+                       f"token {allc['dequant_s']} s, fp64 attention {allc['attention_s']} s, "
+                       f"BLAS on {allc['blas_threads']} threads"),
+            "all_cores": allc, "one_thread": one,
+            "host": {"cpu_model": _cpu_model(), "nproc": os.cpu_count(),
+                     "affinity_cores": ncores, "affinity": f"{aff[0]}-{aff[-1]}" if aff else "",
+                     "blas": blas_name}}
 
 
 # ------------------------------------------------------------------ main ---
@@ -220,11 +268,14 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     # The timed region carries a fixed cost of about 0.6 ms (the first launch
-    # and the closing synchronisations): 3000 steps keep it near 1% of the
-    # headline step loop (0.13 s) and 0.04% of the longest (1.5 s).
+    # and the closing synchronisations): 3000 steps keep it near 0.04% of the
+    # default workload's step loop (about 1.5 s) and 0.5% of the shortest
+    # (the 8K V2-Lite one, 0.13 s).
     ap.add_argument("--steps", type=int, default=3000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=1, help="synthetic workload id (0-5)")
+    ap.add_argument("--config", type=int, default=4,
+                    help="synthetic workload id (0-6); default 4, the largest: 128K cache "
+                         "pressure, B8 H128, append interleaved")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graphs")
     ap.add_argument("--splits", type=int, default=0,

@@ -1,6 +1,7 @@
 // C-ABI host layer of libmla_lowbit.so: argument validation (pure host code,
 // runs before any HIP call), the split plan, and dispatch to the kernels.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -12,7 +13,7 @@
 
 namespace mlb {
 
-static constexpr int kNumCUs = 256;       // MI355X compute units
+static constexpr int kDefaultCUs = 256;   // MI355X compute units (no device visible)
 static constexpr int kWavesTarget = 1;    // resident decode workgroups per CU
 static constexpr int kMinPagesPerSplit = 2;
 static constexpr int kMinPagesPerSplit128 = 8;   // 128-head blocks write 256 KB per split
@@ -21,11 +22,34 @@ static size_t page_bytes_of(int f) {
   return f == MLA_LB_C4R4 ? 20736u : (f == MLA_LB_C2R4 ? 12544u : (f == MLA_LB_C4R4F ? 20992u : 0u));
 }
 
+// Compute units of the current device (a partitioned MI355X exposes fewer
+// than 256), read once per device; kDefaultCUs when no device is visible.
+static int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return kDefaultCUs;
+  }
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n < 1) {
+    (void)hipGetLastError();
+    return kDefaultCUs;
+  }
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 // Split plan.  A max-length sequence of P pages is cut into nsplit splits of
 // pps pages.  Automatic choice: enough (split, sequence, head-block)
-// workgroups to keep every CU busy, but no split shorter than a minimum
-// number of pages (each split costs a heads x 512 fp32 partial write).  Head
-// blocks are 128 rows when use_rows128(H), else 16.
+// workgroups to keep every CU of the current device busy, but no split
+// shorter than a minimum number of pages (each split costs a heads x 512 fp32
+// partial write).  Head blocks are 128 rows when use_rows128(H), else 16.
 
 Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits) {
   Plan p{1, 1, 0};
@@ -37,7 +61,7 @@ Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits) {
   } else {
     const bool h128 = mlb::use_rows128(H);
     const int64_t groups = static_cast<int64_t>(B) * (h128 ? (H + 127) / 128 : H / 16);
-    ns = (static_cast<int64_t>(kNumCUs) * kWavesTarget + groups - 1) / groups;
+    ns = (static_cast<int64_t>(device_cu_count()) * kWavesTarget + groups - 1) / groups;
     const int64_t cap = P / (h128 ? kMinPagesPerSplit128 : kMinPagesPerSplit);
     if (ns > cap) ns = cap;
   }

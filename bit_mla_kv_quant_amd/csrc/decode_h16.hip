@@ -82,8 +82,8 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
   const int n16 = lane & 15, g = lane >> 4;
   const int H = a.H;
 
-  int L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+  const int L_in = a.seq_lens[b];
+  int L = L_in < 0 ? 0 : (L_in > a.max_seq_len ? a.max_seq_len : L_in);
   const int sq = a.seq_slot[b];
   if (sq < 0 || sq >= a.num_seq_slots) L = 0;
   const int npages = (L + PAGE - 1) / PAGE;
@@ -106,7 +106,10 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
   // tokens the lane's row (query row 16hg + n16) attends to: the causal
   // prefix of its query, all L when there is one query per sequence
   const int L_row = L - (a.nq - 1 - (16 * hg + n16) / a.hq);
-  const bool fused = a.new_c != nullptr;
+  // fused writer: token L-1 of a sequence whose length is within bounds (a
+  // clamped length names a token the cache already holds: nothing is stored
+  // or substituted, and the call decodes as mla_decode_lowbit)
+  const bool fused = a.new_c != nullptr && L_in <= a.max_seq_len;
   // fused writer: the middle split of the sequence (first head block)
   // fetches the newest token now and stores it once its own work is done.
   // A middle split holds neither the sink tokens nor the recent window, so

@@ -107,6 +107,68 @@ def _check(fn, code):
         raise MlaLowbitError(fn, code)
 
 
+# ---- argument checks before the C call.  The C layer sees only pointers and
+# the sizes passed with them, so a tensor smaller than its declared shape
+# would be read or written past its end on the device; every tensor's full
+# shape is therefore checked here against the format and (B, nq, H), and all
+# tensors must sit on one GPU.
+def _shape(t, want, name):
+    """want: tuple of ints (exact) or None (any size) per dimension."""
+    if t is None:
+        raise ValueError(f"{name}: missing")
+    got = tuple(t.shape)
+    if len(got) != len(want) or any(w is not None and g != w for g, w in zip(got, want)):
+        shown = tuple("*" if w is None else w for w in want)
+        raise ValueError(f"{name}: shape {got}, expected {shown}")
+
+
+def _rows_at_least(t, n, name):
+    if t is None:
+        raise ValueError(f"{name}: missing")
+    if t.dim() < 1 or t.shape[0] < n:
+        raise ValueError(f"{name}: needs at least {n} rows, has shape {tuple(t.shape)}")
+
+
+def _same_gpu(fn, *named):
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{fn}: {name} must be a GPU tensor (device {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{fn}: {name} is on {t.device}, other tensors on {dev}")
+
+
+def _cache_shapes(fmt, pages, prot):
+    pb = _lib.mla_lb_page_bytes(_fmt(fmt))
+    if pb == 0:
+        raise ValueError(f"unknown cache format {fmt!r}")
+    _shape(pages, (None, pb), "pages")
+    _shape(prot, (None, 132, 576), "prot")
+
+
+def _decode_shapes(fmt, q_lat, q_rope, pages, prot, seq_slot, block_table, seq_lens, out, lse,
+                   lead):
+    """lead: the leading query dims, (B, H) or (B, nq, H)."""
+    B = lead[0]
+    _shape(q_lat, lead + (512,), "q_lat")
+    _shape(q_rope, lead + (64,), "q_rope")
+    _cache_shapes(fmt, pages, prot)
+    _rows_at_least(seq_slot, B, "seq_slot")
+    _shape(seq_slot, (None,), "seq_slot")
+    _shape(block_table, (None, None), "block_table")
+    _rows_at_least(block_table, B, "block_table")
+    _rows_at_least(seq_lens, B, "seq_lens")
+    _shape(seq_lens, (None,), "seq_lens")
+    if out is not None:
+        _shape(out, lead + (512,), "out")
+    if lse is not None:
+        _shape(lse, lead, "lse")
+
+
 def mla_lb_version():
     return _lib.mla_lb_version()
 
@@ -129,6 +191,15 @@ def kv_quant_append(fmt, latent, k_rope, slot_mapping, seq_slot, pos, new_len, p
     slot_mapping int64 [T]; seq_slot, pos, new_len int32 [T];
     pages uint8 [num_pages, page_bytes]; prot bf16 [num_seq_slots, 132, 576]."""
     T = latent.shape[0]
+    _shape(latent, (T, 512), "latent")
+    _shape(k_rope, (T, 64), "k_rope")
+    for name, t in (("slot_mapping", slot_mapping), ("seq_slot", seq_slot), ("pos", pos),
+                    ("new_len", new_len)):
+        _shape(t, (T,), name)
+    _cache_shapes(fmt, pages, prot)
+    _same_gpu("kv_quant_append", ("latent", latent), ("k_rope", k_rope),
+              ("slot_mapping", slot_mapping), ("seq_slot", seq_slot), ("pos", pos),
+              ("new_len", new_len), ("pages", pages), ("prot", prot))
     code = _lib.kv_quant_append(
         _fmt(fmt), _ptr(latent, _BF16, "latent"), _ptr(k_rope, _BF16, "k_rope"),
         _ptr(slot_mapping, (torch.int64,), "slot_mapping"),
@@ -151,7 +222,14 @@ def mla_decode_lowbit(fmt, q_lat, q_rope, pages, prot, seq_slot, block_table, se
                       max_seq_len, softmax_scale, num_splits=0, workspace=None, out=None,
                       lse=None, stream=None):
     """Decode attention; returns (out fp32 [B,H,512], lse fp32 [B,H])."""
+    if q_lat.dim() != 3:
+        raise ValueError(f"q_lat: shape {tuple(q_lat.shape)}, expected (B, H, 512)")
     B, H = q_lat.shape[0], q_lat.shape[1]
+    _decode_shapes(fmt, q_lat, q_rope, pages, prot, seq_slot, block_table, seq_lens, out, lse,
+                   (B, H))
+    _same_gpu("mla_decode_lowbit", ("q_lat", q_lat), ("q_rope", q_rope), ("pages", pages),
+              ("prot", prot), ("seq_slot", seq_slot), ("block_table", block_table),
+              ("seq_lens", seq_lens), ("workspace", workspace), ("out", out), ("lse", lse))
     dev = q_lat.device
     if out is None:
         out = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
@@ -180,10 +258,18 @@ def mla_decode_lowbit_append(fmt, latent, k_rope, q_lat, q_rope, pages, prot, se
     """One decode step with the cache writer fused in: stores the newest token
     (latent [B,512], k_rope [B,64] bf16 at position seq_lens[b]-1) into pages
     and prot, then decodes; returns (out fp32 [B,H,512], lse fp32 [B,H])."""
+    if q_lat.dim() != 3:
+        raise ValueError(f"q_lat: shape {tuple(q_lat.shape)}, expected (B, H, 512)")
     B, H = q_lat.shape[0], q_lat.shape[1]
+    _shape(latent, (B, 512), "latent")       # one new token per sequence
+    _shape(k_rope, (B, 64), "k_rope")
+    _decode_shapes(fmt, q_lat, q_rope, pages, prot, seq_slot, block_table, seq_lens, out, lse,
+                   (B, H))
+    _same_gpu("mla_decode_lowbit_append", ("latent", latent), ("k_rope", k_rope),
+              ("q_lat", q_lat), ("q_rope", q_rope), ("pages", pages), ("prot", prot),
+              ("seq_slot", seq_slot), ("block_table", block_table), ("seq_lens", seq_lens),
+              ("workspace", workspace), ("out", out), ("lse", lse))
     dev = q_lat.device
-    if latent.shape[0] != B or k_rope.shape[0] != B:
-        raise ValueError("latent / k_rope need one row per sequence")
     if out is None:
         out = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
     if lse is None:
@@ -220,7 +306,14 @@ def mla_decode_lowbit_mq(fmt, q_lat, q_rope, pages, prot, seq_slot, block_table,
     """Attention of the last nq tokens of each sequence over their causal
     prefixes.  q_lat [B,nq,H,512], q_rope [B,nq,H,64] bf16; returns
     (out fp32 [B,nq,H,512], lse fp32 [B,nq,H])."""
+    if q_lat.dim() != 4:
+        raise ValueError(f"q_lat: shape {tuple(q_lat.shape)}, expected (B, nq, H, 512)")
     B, nq, H = q_lat.shape[0], q_lat.shape[1], q_lat.shape[2]
+    _decode_shapes(fmt, q_lat, q_rope, pages, prot, seq_slot, block_table, seq_lens, out, lse,
+                   (B, nq, H))
+    _same_gpu("mla_decode_lowbit_mq", ("q_lat", q_lat), ("q_rope", q_rope), ("pages", pages),
+              ("prot", prot), ("seq_slot", seq_slot), ("block_table", block_table),
+              ("seq_lens", seq_lens), ("workspace", workspace), ("out", out), ("lse", lse))
     dev = q_lat.device
     if out is None:
         out = torch.empty((B, nq, H, 512), dtype=torch.float32, device=dev)
@@ -268,6 +361,13 @@ def mla_lb_smooth_scales(stat, alpha, pair_tied=False):
 
 def mla_lb_dequant_dump(fmt, pages, page_id, out=None, stream=None):
     """bf16 bits [64, 576] (int16) reconstructed by the decode kernel for one page."""
+    pb = _lib.mla_lb_page_bytes(_fmt(fmt))
+    if pb == 0:
+        raise ValueError(f"unknown cache format {fmt!r}")
+    _shape(pages, (None, pb), "pages")
+    if out is not None:
+        _shape(out, (64, 576), "out")
+    _same_gpu("mla_lb_dequant_dump", ("pages", pages), ("out", out))
     if out is None:
         out = torch.empty((64, 576), dtype=torch.int16, device=pages.device)
     _check("mla_lb_dequant_dump",

@@ -23,6 +23,14 @@
  *     outside the sizes passed in are skipped (never dereferenced).  Such
  *     inputs give unspecified results, not memory faults.  NaN/Inf inputs and
  *     overlapping slots are outside the defined domain.
+ *   - Numeric domain of the decode calls: the softmax keeps one reference
+ *     maximum per head and split, fixed by its first tile, and lets later
+ *     weights exp(S - reference) grow up to 2^64 before the reference is
+ *     raised (the split is then redone; the result is the same single
+ *     softmax).  The fp32 sums of weighted latent values therefore need
+ *     |c~_i| * seq_len < 2^63 (about 9.2e18) to stay finite -- 2^64 less
+ *     headroom than a softmax rescaled at every tile.  Within that domain
+ *     every finite input gives finite outputs.
  *
  * Cache format (one physical page = 64 token slots; slot = page*64 + offset)
  *   [QuantMLA App. C.4/C.5], [MLA blog §6].  Structure-of-arrays, every
@@ -138,8 +146,11 @@ int kv_quant_append(int f, const uint16_t* latent, const uint16_t* k_rope,
 
 /*
  * mla_decode_lowbit_workspace -- bytes of workspace mla_decode_lowbit needs
- * for the same (f, B, H, max_seq_len, num_splits) (host, pure).  Zero when
- * the call runs in one pass (a single split per sequence).
+ * for the same (f, B, H, max_seq_len, num_splits) (host).  Zero when the
+ * call runs in one pass (a single split per sequence).  The automatic plan
+ * (num_splits = 0) sizes itself to the compute units of the current HIP
+ * device (256 when no device is visible), so query it with the device the
+ * decode call will run on current.
  *   bytes (host out)
  */
 int mla_decode_lowbit_workspace(int f, int32_t B, int32_t H, int32_t max_seq_len,
@@ -173,8 +184,9 @@ int mla_decode_lowbit_workspace(int f, int32_t B, int32_t H, int32_t max_seq_len
  *   max_seq_len  host upper bound of seq_lens (sizes the split plan)
  *   B >= 1; H a multiple of 16, 16 <= H <= 128
  *   softmax_scale  > 0, finite
- *   num_splits   0 = automatic, else the number of splits a max_seq_len
- *                sequence is cut into (>= 1)
+ *   num_splits   0 = automatic (enough splits to occupy every compute unit
+ *                of the current device, none shorter than a few pages), else
+ *                the number of splits a max_seq_len sequence is cut into (>= 1)
  *   workspace    device buffer of at least mla_decode_lowbit_workspace(...)
  *                bytes (may be NULL when that size is 0)
  *   out          [B][H][512] fp32
@@ -209,7 +221,11 @@ int mla_decode_lowbit(int f, const uint16_t* q_lat, const uint16_t* q_rope,
  *   other arguments, workspace size and errors: as mla_decode_lowbit.
  * Sequences with L = 0 append nothing; a block-table entry outside
  * [0, num_pages) for block (L-1)/64 stores nothing (that token then reads as
- * an unusable slot, as in mla_decode_lowbit).
+ * an unusable slot, as in mla_decode_lowbit).  A sequence whose seq_lens[b]
+ * exceeds min(max_seq_len, max_blocks*64) appends nothing either: its length
+ * is clamped as in mla_decode_lowbit, the clamped last token is one the
+ * cache already holds, and that sequence's result is exactly
+ * mla_decode_lowbit's (pages and prot untouched).
  */
 int mla_decode_lowbit_append(int f, const uint16_t* latent, const uint16_t* k_rope,
                              const uint16_t* q_lat, const uint16_t* q_rope, uint8_t* pages,
@@ -222,7 +238,8 @@ int mla_decode_lowbit_append(int f, const uint16_t* latent, const uint16_t* k_ro
 
 /*
  * mla_decode_lowbit_mq_workspace -- bytes of workspace mla_decode_lowbit_mq
- * needs for the same (f, B, nq, H, max_seq_len, num_splits) (host, pure).
+ * needs for the same (f, B, nq, H, max_seq_len, num_splits) (host; the
+ * automatic plan reads the current device as mla_decode_lowbit_workspace).
  *   bytes (host out)
  */
 int mla_decode_lowbit_mq_workspace(int f, int32_t B, int32_t nq, int32_t H,

@@ -233,3 +233,113 @@ int main(void) {
                     "-I", os.path.join(ROOT, "include"), str(src), "-L", libdir, "-lmla_lowbit",
                     f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
     assert subprocess.run([str(exe)]).returncode == 0
+
+
+# ------------------------------------------- binding-side shape validation ---
+def _decode_tensors(fmt="C4R4", B=2, H=16, nq=None, num_pages=4, max_blocks=3):
+    import torch
+    from bit_mla_kv_quant_amd import ops as o
+    lead = (B, H) if nq is None else (B, nq, H)
+    return dict(
+        q_lat=torch.zeros(lead + (512,), dtype=torch.int16),
+        q_rope=torch.zeros(lead + (64,), dtype=torch.int16),
+        pages=torch.zeros((num_pages, o.mla_lb_page_bytes(fmt)), dtype=torch.uint8),
+        prot=torch.zeros((B, 132, 576), dtype=torch.int16),
+        seq_slot=torch.zeros(B, dtype=torch.int32),
+        block_table=torch.zeros((B, max_blocks), dtype=torch.int32),
+        seq_lens=torch.zeros(B, dtype=torch.int32),
+        out=torch.zeros(lead + (512,), dtype=torch.float32),
+        lse=torch.zeros(lead, dtype=torch.float32))
+
+
+def _call_decode(ops, fmt, t, nq=False):
+    fn = ops.mla_decode_lowbit_mq if nq else ops.mla_decode_lowbit
+    return fn(fmt, t["q_lat"], t["q_rope"], t["pages"], t["prot"], t["seq_slot"],
+              t["block_table"], t["seq_lens"], 100, 0.07, out=t["out"], lse=t["lse"])
+
+
+@pytest.mark.parametrize("bad, msg", [
+    ("pages_width", "pages"),        # a C4R4F call on a pool sized for C4R4
+    ("prot_rows", "prot"),
+    ("short_block_table", "block_table"),
+    ("short_seq_lens", "seq_lens"),
+    ("q_rope", "q_rope"),
+    ("out", "out"),
+    ("lse", "lse"),
+])
+def test_binding_rejects_mismatched_shapes(ops, bad, msg):
+    """The binding checks every tensor's full shape against the format and
+    (B, H) before the C call: the C layer only sees pointers, and a short
+    tensor would be read or written past its end on the device."""
+    import torch
+    fmt = "C4R4F" if bad == "pages_width" else "C4R4"
+    t = _decode_tensors("C4R4" if bad == "pages_width" else fmt)
+    if bad == "prot_rows":
+        t["prot"] = torch.zeros((2, 131, 576), dtype=torch.int16)
+    elif bad == "short_block_table":
+        t["block_table"] = torch.zeros((1, 3), dtype=torch.int32)
+    elif bad == "short_seq_lens":
+        t["seq_lens"] = torch.zeros(1, dtype=torch.int32)
+    elif bad == "q_rope":
+        t["q_rope"] = torch.zeros((2, 16, 32), dtype=torch.int16)
+    elif bad == "out":
+        t["out"] = torch.zeros((2, 8, 512), dtype=torch.float32)
+    elif bad == "lse":
+        t["lse"] = torch.zeros((2,), dtype=torch.float32)
+    with pytest.raises(ValueError, match=msg):
+        _call_decode(ops, fmt, t)
+
+
+def test_binding_rejects_bad_shapes_on_every_entry_point(ops):
+    import torch
+    t = _decode_tensors(nq=4)
+    t["q_rope"] = torch.zeros((2, 4, 16, 63), dtype=torch.int16)
+    with pytest.raises(ValueError, match="q_rope"):
+        _call_decode(ops, "C4R4", t, nq=True)
+    t = _decode_tensors()
+    lat, kr = torch.zeros((2, 512), dtype=torch.int16), torch.zeros((1, 64), dtype=torch.int16)
+    with pytest.raises(ValueError, match="k_rope"):
+        ops.mla_decode_lowbit_append("C4R4", lat, kr, t["q_lat"], t["q_rope"], t["pages"],
+                                     t["prot"], t["seq_slot"], t["block_table"], t["seq_lens"],
+                                     100, 0.07)
+    T = 3
+    args = [torch.zeros((T, 512), dtype=torch.int16), torch.zeros((T, 64), dtype=torch.int16),
+            torch.zeros(T, dtype=torch.int64), torch.zeros(T, dtype=torch.int32),
+            torch.zeros(T - 1, dtype=torch.int32), torch.zeros(T, dtype=torch.int32)]
+    with pytest.raises(ValueError, match="pos"):
+        ops.kv_quant_append("C2R4", *args, t["pages"], t["prot"])   # also a C4R4-sized pool
+    with pytest.raises(ValueError, match="pages"):
+        ops.mla_lb_dequant_dump("C2R4", t["pages"], 0)
+
+
+def test_binding_requires_gpu_tensors(ops):
+    """Correct shapes on the host are refused before the C call: every tensor
+    must sit on one GPU."""
+    t = _decode_tensors()
+    with pytest.raises(ValueError, match="GPU tensor"):
+        _call_decode(ops, "C4R4", t)
+
+
+def test_host_layer_under_address_and_ub_sanitizers(tmp_path):
+    """abi.cpp (validation, split plan, workspace sizing, calibration helpers)
+    built for the host with AddressSanitizer and UndefinedBehaviorSanitizer,
+    the kernel launchers replaced by stubs, and driven through every host
+    path by tests/native/abi_host_check.cpp; any memory error, leak or
+    undefined behaviour aborts the run.  Device code is built without
+    sanitizers (each -fsanitize= applies to the host pass only)."""
+    exe = tmp_path / "abi_host_check"
+    cmd = ["/opt/rocm/bin/hipcc", "-x", "hip", "--offload-arch=gfx950", "-std=c++17", "-O1", "-g",
+           "-fno-omit-frame-pointer",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all",
+           os.path.join(ROOT, "bit_mla_kv_quant_amd", "csrc", "abi.cpp"),
+           os.path.join(ROOT, "tests", "native", "abi_host_check.cpp"), "-o", str(exe)]
+    if not os.path.exists(cmd[0]):
+        pytest.skip("hipcc not available")
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0",
+               UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-4000:])
+    assert "abi host checks passed" in r.stdout

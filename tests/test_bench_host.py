@@ -85,3 +85,23 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+def test_cpu_baseline_reports_both_thread_counts_and_phases():
+    """The CPU leg times the oracle twice -- BLAS on every core of the
+    affinity set, then on one thread -- with unpack + dequantize and fp64
+    attention reported apart, and records the host it ran on."""
+    from bit_mla_kv_quant_amd import synth
+    d = synth.draw(synth.WORKLOADS[0])
+    r = bench.cpu_baseline(d, "C4R4", budget_s=0.2, budget_1t_s=0.2)
+    for k in ("value", "unit", "cores", "kind", "sample"):
+        assert k in r
+    assert r["kind"] == "oracle" and r["unit"] == "KV-tokens/s"
+    assert r["one_thread"]["blas_threads"] == 1
+    assert r["cores"] == r["all_cores"]["blas_threads"] >= 1
+    for leg in (r["all_cores"], r["one_thread"]):
+        assert leg["dequant_s"] > 0 and leg["attention_s"] > 0 and leg["tokens"] >= 1024
+        assert leg["kv_tokens_per_s"] == pytest.approx(
+            leg["tokens"] / (leg["dequant_s"] + leg["attention_s"]), rel=1e-2)
+    assert r["host"]["affinity_cores"] == len(os.sched_getaffinity(0))
+    assert r["host"]["cpu_model"]

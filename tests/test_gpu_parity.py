@@ -1,9 +1,11 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
 Bars: packed page bytes and protection rows bit-exact; reconstructed bf16
-rows bit-exact; attention output within 2e-3 relative L2 per sequence and
-log-sum-exp within 1e-3 absolute (fp32 accumulation of bf16 MFMA products
-with bf16 attention weights).
+rows bit-exact; attention output within 2e-3 relative L2 for every
+(sequence, head) row -- and every (sequence, query, head) row with several
+queries -- and log-sum-exp within 1e-3 absolute (fp32 accumulation of bf16
+MFMA products with bf16 hi + lo attention weights).  Different split plans of
+one call agree within 1e-5 per row and 1e-5 in log-sum-exp.
 """
 
 import numpy as np
@@ -12,13 +14,20 @@ import pytest
 from bit_mla_kv_quant_amd import synth
 from oracle import attention, layout, quant
 
-from gpu_helpers import GpuCache, oracle_decode, oracle_decode_mq, oracle_page, rel_l2, t_bf16, t_i32
+from gpu_helpers import GpuCache, oracle_decode, oracle_decode_mq, oracle_page, t_bf16, t_i32
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 TOL_OUT = 2e-3
 TOL_LSE = 1e-3
+TOL_SPLIT = 1e-5
+
+
+def rel_l2_rows(a, b):
+    """rel-L2 of each row (last axis: the 512 latent dims) of a against b."""
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return np.linalg.norm(a - b, axis=-1) / np.maximum(np.linalg.norm(b, axis=-1), 1e-30)
 
 
 def say(*a):
@@ -26,6 +35,8 @@ def say(*a):
 
 
 def check_decode(d, cache, out, lse, lens, which=None, fmt=None):
+    """Every (sequence, head) row within TOL_OUT rel-L2 of the oracle and its
+    lse within TOL_LSE; returns the worst row."""
     worst = 0.0
     for b in (range(d.B) if which is None else which):
         L = int(lens[b])
@@ -33,9 +44,9 @@ def check_decode(d, cache, out, lse, lens, which=None, fmt=None):
         if L == 0:
             assert np.all(out[b] == 0) and np.all(np.isneginf(lse[b])), b
             continue
-        e = rel_l2(out[b], ro)
-        worst = max(worst, e)
-        assert e <= TOL_OUT, (b, L, e)
+        e = rel_l2_rows(out[b], ro)
+        worst = max(worst, float(e.max()))
+        assert np.all(e <= TOL_OUT), (b, L, int(e.argmax()), float(e.max()))
         assert np.max(np.abs(lse[b] - rl)) <= TOL_LSE, (b, L, np.max(np.abs(lse[b] - rl)))
     return worst
 
@@ -130,7 +141,7 @@ def test_decode_huge_scale_groups(fmt, H):
         for b in range(d.B):
             L = int(d.lens[b])
             ro, rl = oracle_decode(d, b, L)
-            assert rel_l2(out[b], ro) <= TOL_OUT, (b, rel_l2(out[b], ro))
+            assert np.all(rel_l2_rows(out[b], ro) <= TOL_OUT), (b, rel_l2_rows(out[b], ro).max())
             # scores of ~1e35 are fp32 sums of 576 products that cancel: their
             # error is bounded by gamma_576 * sum |q_j x_j| (gamma_576 < 1e-4),
             # so the lse bar grows with that magnitude
@@ -164,17 +175,22 @@ def test_split_invariance_and_determinism(fmt):
     c = GpuCache(d)
     c.fill()
     # Every partition meets the oracle bar.  Partitions are not bitwise equal:
-    # attention weights are rounded to bf16 relative to each split's running
-    # max, so results agree to the bf16-weight rounding level.
+    # the weights enter the MFMAs as bf16 hi + lo pairs relative to each
+    # split's reference maximum (about 2^-17 relative per weight), and the
+    # split sums are added in another order, so plans agree to about 1e-6.
     ref_out, ref_lse = c.decode(num_splits=1)
     check_decode(d, c, ref_out, ref_lse, d.lens)
     for ns in (2, 7, 0, 64):
         out, lse = c.decode(num_splits=ns)
         w = check_decode(d, c, out, lse, d.lens)
-        say("  num_splits", ns, "worst rel-L2 vs oracle", f"{w:.2e}")
+        worst_split = 0.0
         for b in range(d.B):
-            assert rel_l2(out[b], ref_out[b]) <= TOL_OUT
-        assert np.max(np.abs(lse - ref_lse)) <= 2e-5
+            e = rel_l2_rows(out[b], ref_out[b])
+            worst_split = max(worst_split, float(e.max()))
+            assert np.all(e <= TOL_SPLIT), (ns, b, int(e.argmax()), float(e.max()))
+        say("  num_splits", ns, "worst rel-L2 vs oracle", f"{w:.2e}",
+            "vs one split", f"{worst_split:.2e}")
+        assert np.max(np.abs(lse - ref_lse)) <= TOL_SPLIT
     # a fixed plan is deterministic
     for ns in (1, 0):
         o1, l1 = c.decode(num_splits=ns)
@@ -234,7 +250,7 @@ def test_token_aging(fmt):
         c.append([0], [np.array([L - 1])], [L])
         out, lse = c.decode(lens=[L])
         ro, rl = oracle_decode(d, 0, L)
-        assert rel_l2(out[0], ro) <= TOL_OUT, L
+        assert np.all(rel_l2_rows(out[0], ro) <= TOL_OUT), L
         assert np.max(np.abs(lse[0] - rl)) <= TOL_LSE, L
         if L % 50 == 0:
             pages = c.pages.cpu().numpy()
@@ -281,6 +297,32 @@ def test_fused_step_equals_append_then_decode(fmt, H):
         np.testing.assert_array_equal(pages[pid], oracle_page(d, pid, lens), err_msg=f"page {pid}")
 
 
+@pytest.mark.parametrize("H", [16, 128])
+def test_fused_step_skips_lengths_beyond_bound(H):
+    """A fused call whose seq_lens[b] is max_seq_len + 1 stores nothing for
+    that sequence (the clamped last token is already cached): its page bytes
+    and protection rows are unchanged, and the whole call equals
+    kv_quant_append of the in-bound sequence's token followed by
+    mla_decode_lowbit with the same lengths, bit for bit."""
+    d = synth.small(fmt="C4R4", batch=2, heads=H, lens=(300, 700), seed=73, extra_tokens=300)
+    say("fused beyond bound", H)
+    base = GpuCache(d)
+    base.fill()
+    torch.cuda.synchronize()
+    lens = np.array([301, 701])
+    for ns in (0, 1):
+        sep, fus = base.clone(), base.clone()
+        sep.append([0], [np.array([300])], [301])
+        o1, l1 = sep.decode(lens=lens, num_splits=ns, max_seq_len=700)
+        o2, l2 = fus.fused_step(lens, num_splits=ns, max_seq_len=700)
+        np.testing.assert_array_equal(fus.pages.cpu().numpy(), sep.pages.cpu().numpy())
+        np.testing.assert_array_equal(fus.prot.cpu().numpy(), sep.prot.cpu().numpy())
+        np.testing.assert_array_equal(fus.prot.cpu().numpy()[1], base.prot.cpu().numpy()[1])
+        np.testing.assert_array_equal(o2, o1)
+        np.testing.assert_array_equal(l2, l1)
+        check_decode(d, fus, o2, l2, [301, 700])
+
+
 @pytest.mark.parametrize("fmt", ["C4R4", "C2R4"])
 def test_fused_token_aging(fmt):
     """One fused step per token from L=1 to 260: every step matches the
@@ -307,9 +349,9 @@ def check_decode_mq(d, out, lse, lens, which=None, fmt=None):
             if L - d.wl.queries + 1 + j <= 0:      # empty causal prefix
                 assert np.all(out[b, j] == 0) and np.all(np.isneginf(lse[b, j])), (b, j)
                 continue
-            e = rel_l2(out[b, j], ro[j])
-            worst = max(worst, e)
-            assert e <= TOL_OUT, (b, L, j, e)
+            e = rel_l2_rows(out[b, j], ro[j])
+            worst = max(worst, float(e.max()))
+            assert np.all(e <= TOL_OUT), (b, L, j, int(e.argmax()), float(e.max()))
             assert np.max(np.abs(lse[b, j] - rl[j])) <= TOL_LSE, (b, L, j)
     return worst
 

@@ -320,3 +320,102 @@ def test_page_sizes():
     assert layout.page_bytes("C2R4") == 12544
     assert layout.page_bytes("C4R4F") == 20992       # 328 B/token against the pages' 320
     assert layout.PROT_ROWS * 576 * 2 == 152064
+
+
+# ------------------------------------------- page byte placement (known answer) ---
+def _hand_token(fmt):
+    """One token with hand-chosen codes and metadata (not from the quantizer):
+    content code of dim d = (7d + 3) mod 16 (C4R4) or (3d + 1) mod 4 (C2R4),
+    RoPE code of dim j = (5j + 1) mod 16, group g (0..7) scale bits 0x3C00+g
+    and zero bits 0xBF80+g, RoPE group scale 0x3D11 and zero 0xC022."""
+    d = np.arange(512)
+    cc = (7 * d + 3) % 16 if fmt == "C4R4" else (3 * d + 1) % 4
+    qt = {"codes_c": cc.astype(np.uint8)[None, :],
+          "codes_r": ((5 * np.arange(64) + 1) % 16).astype(np.uint8)[None, :],
+          "scale": np.array([[0x3C00 + g for g in range(8)] + [0x3D11]], np.uint16),
+          "zero": np.array([[0xBF80 + g for g in range(8)] + [0xC022]], np.uint16)}
+    return cc, qt
+
+
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4"])
+def test_page_byte_placement_known_answer(fmt):
+    """A token written at slot 5 of page 1 lands at the absolute byte offsets
+    the header's layout gives, computed here by hand: content block b at
+    (b*64 + 5)*64, codes_r at OFF_R + 5*32, meta_c (scale, zero) of group g at
+    OFF_MC + 5*32 + 4g (little-endian bf16 pairs), meta_r at OFF_MR + 5*4; no
+    other byte of the pool changes."""
+    cc, qt = _hand_token(fmt)
+    pb = layout.page_bytes(fmt)
+    pages = np.zeros((2, pb), np.uint8)
+    layout.write_tokens(pages, np.array([64 + 5]), qt, fmt)
+    assert not pages[0].any()
+    pg = pages[1]
+    want = np.zeros(pb, np.uint8)
+    if fmt == "C4R4":
+        OFF_R, OFF_MC, OFF_MR = 16384, 18432, 20480
+        for b in range(4):                           # byte k: dims 128b+2k (lo), +2k+1 (hi)
+            for k in range(64):
+                want[(b * 64 + 5) * 64 + k] = cc[128 * b + 2 * k] | (cc[128 * b + 2 * k + 1] << 4)
+        # spot values by hand: dims 0, 1 -> codes 3, 10 -> 0xA3; dims 384, 385
+        # (block 3, byte 0) -> (2688+3)%16 = 3, (2695+3)%16 = 10 -> 0xA3;
+        # dims 130, 131 (block 1, byte 1) -> 1, 8 -> 0x81
+        assert pg[320] == 0xA3 and pg[(3 * 64 + 5) * 64] == 0xA3
+        assert pg[(1 * 64 + 5) * 64 + 1] == 0x81
+    else:
+        OFF_R, OFF_MC, OFF_MR = 8192, 10240, 12288
+        for b in range(2):                           # 32-bit word k: dims 256b+16k..+15
+            for k in range(16):
+                w = 0
+                for m in range(8):
+                    w |= int(cc[256 * b + 16 * k + 2 * m]) << (2 * m)
+                    w |= int(cc[256 * b + 16 * k + 2 * m + 1]) << (16 + 2 * m)
+                off = (b * 64 + 5) * 64 + 4 * k
+                want[off:off + 4] = [w & 0xFF, (w >> 8) & 0xFF, (w >> 16) & 0xFF, w >> 24]
+        # by hand: dims 0..15 carry codes 1,0,3,2,...: even dims 1,3,1,3 ->
+        # 0xDDDD, odd dims 0,2,0,2 -> 0x8888; word 0x8888DDDD, bytes DD DD 88 88
+        assert bytes(pg[320:324]) == bytes([0xDD, 0xDD, 0x88, 0x88])
+    for k in range(32):                              # codes_r: dims 2k (lo), 2k+1 (hi)
+        r0, r1 = (10 * k + 1) % 16, (10 * k + 6) % 16
+        want[OFF_R + 5 * 32 + k] = r0 | (r1 << 4)
+    assert pg[OFF_R + 160] == 0x61                   # RoPE dims 0, 1 -> codes 1, 6
+    for g in range(8):
+        s, z = 0x3C00 + g, 0xBF80 + g
+        want[OFF_MC + 5 * 32 + 4 * g:OFF_MC + 5 * 32 + 4 * g + 4] = [s & 0xFF, s >> 8, z & 0xFF, z >> 8]
+    want[OFF_MR + 20:OFF_MR + 24] = [0x11, 0x3D, 0x22, 0xC0]
+    assert bytes(pg[OFF_MC + 160 + 12:OFF_MC + 160 + 16]) == bytes([0x03, 0x3C, 0x83, 0xBF])
+    np.testing.assert_array_equal(pg, want)
+    # and read_page, the oracle's inverse, returns the hand-chosen values
+    back = layout.read_page(pg, fmt)
+    for k in ("codes_c", "codes_r", "scale", "zero"):
+        np.testing.assert_array_equal(back[k][5], qt[k][0])
+
+
+# ------------------------------------- round-trip bounds on what is multiplied ---
+@pytest.mark.parametrize("bits", [2, 4])
+def test_roundtrip_bound_on_bf16_reconstruction(bits):
+    """Two bounds, both asserted.  The quantizer's own round trip (exact
+    q*s + z) stays within s/2 of x -- the per-element bound of the
+    quantization itself.  The value the decode multiplies is the stored bf16
+    reconstruction x^ = bf16(fl32(q*s + z)), which adds at most one fp32 and
+    one bf16 rounding: |x - x^| <= s/2 + ulp_bf16(x^)/2 + 2^-24 |x^|.  The
+    bf16 step alone can exceed s/2 (lo = 64, x = 64.5, hi = 76: s = 0.80078,
+    q = 1, x^ = 65.0, error 0.5 > 0.40), so the first bound is not asserted
+    on x^."""
+    rng = np.random.default_rng(40 + bits)
+    a = np.exp(0.5 * rng.standard_normal(64))
+    a[:2] *= 16.0
+    x64 = rng.standard_normal((20000, 64)) * a + rng.standard_normal((20000, 1)) * 40.0
+    xb = quant.f32_to_bf16(x64.astype(np.float32))
+    hand = quant.f32_to_bf16(np.array([[64.0, 64.5, 76.0] + [70.0] * 61], np.float32))
+    xb = np.concatenate([hand, xb])
+    q, sb, zb = quant.quantize_groups(xb, bits)
+    x = quant.bf16_to_f32(xb).astype(np.float64)
+    s = quant.bf16_to_f32(sb).astype(np.float64)[:, None]
+    exact = q * s + quant.bf16_to_f32(zb).astype(np.float64)[:, None]
+    assert np.all(np.abs(x - exact) <= 0.5 * s * (1 + 1e-6))
+    xh = quant.bf16_to_f32(quant.dequantize_groups(q, sb, zb)).astype(np.float64)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(xh), 1e-300))) - 7)
+    assert np.all(np.abs(x - xh) <= 0.5 * s + 0.5 * ulp + np.abs(xh) * 2.0 ** -24)
+    if bits == 4:                                    # the hand case, both ways
+        assert xh[0, 1] == 65.0 and abs(x[0, 1] - xh[0, 1]) > 0.5 * s[0, 0]
+    assert np.any(np.abs(x - xh)[1:] > 0.5 * s[1:])  # the bf16 step does matter

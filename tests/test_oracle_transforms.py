@@ -85,3 +85,27 @@ def test_alpha_search_lowers_error_on_outlier_channels(path):
     assert errs[al] < 0.9 * errs[0.0], errs
     if path == "rope":
         assert np.all(s[0::2] == s[1::2])
+
+
+@pytest.mark.parametrize("path", ["content", "rope"])
+def test_alpha_search_exact_tie_keeps_smallest_alpha(path):
+    """[QuantMLA App. C.4]: a tie favours the smaller alpha.  Calibration rows
+    whose every channel has statistic exactly 1 give the scale 1^-alpha = 1
+    for every candidate, so all candidates tie exactly; the search must keep
+    the smallest (0), not the first or last it tried."""
+    rng = np.random.default_rng(5)
+    d = synth.small(fmt="C4R4", batch=2, heads=4, lens=(300, 300), seed=5)
+    calib_c = quant.f32_to_bf16(rng.choice([-1.0, 1.0], size=(200, 512)).astype(np.float32))
+    calib_kr = quant.f32_to_bf16(rng.choice([-1.0, 1.0], size=(200, 64)).astype(np.float32))
+    heldout = [(d.c[b], d.kr[b], d.q_lat[b], d.q_rope[b]) for b in (0, 1)]
+    order = list(transforms.ALPHAS)
+    for alphas in (order, order[::-1]):               # candidate order does not matter
+        saved = transforms.ALPHAS
+        transforms.ALPHAS = tuple(alphas)
+        try:
+            al, errs, s = transforms.select_alpha(calib_c, calib_kr, heldout, "C4R4", d.scale, path)
+        finally:
+            transforms.ALPHAS = saved
+        assert len(set(errs.values())) == 1, errs    # an exact tie
+        assert al == min(order) == 0.0
+        assert np.all(s == 1.0)
