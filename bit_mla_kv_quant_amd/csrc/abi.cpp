@@ -288,6 +288,30 @@ int mla_lb_smooth_scales(const float* stat, int32_t n, float alpha, int32_t pair
   return MLA_LB_OK;
 }
 
+int mla_lb_hadamard_rows(const float* x, int64_t rows, int32_t n, float* y) {
+  if (!x || !y) return MLA_LB_EINVAL;
+  if (rows < 1 || n < 1 || n > (1 << 20) || (n & (n - 1)) != 0) return MLA_LB_ESHAPE;
+  // y[r] = x[r] H_n with H_n Sylvester's +-1 matrix / sqrt(n): the in-place
+  // butterfly over doubling strides builds [[H, H], [H, -H]] at every level;
+  // H_n is symmetric, so the row-vector product equals H_n x[r]^T
+  std::vector<double> v(static_cast<size_t>(n));
+  const double norm = 1.0 / std::sqrt(static_cast<double>(n));
+  for (int64_t r = 0; r < rows; ++r) {
+    const float* xr = x + r * n;
+    for (int32_t i = 0; i < n; ++i) v[static_cast<size_t>(i)] = xr[i];
+    for (int32_t len = 1; len < n; len <<= 1)
+      for (int32_t i = 0; i < n; i += 2 * len)
+        for (int32_t k = i; k < i + len; ++k) {
+          const double a = v[static_cast<size_t>(k)], b = v[static_cast<size_t>(k + len)];
+          v[static_cast<size_t>(k)] = a + b;
+          v[static_cast<size_t>(k + len)] = a - b;
+        }
+    float* yr = y + r * n;
+    for (int32_t i = 0; i < n; ++i) yr[i] = static_cast<float>(v[static_cast<size_t>(i)] * norm);
+  }
+  return MLA_LB_OK;
+}
+
 int mla_lb_dequant_dump(int f, const uint8_t* pages, int64_t num_pages, int64_t page_id,
                         uint16_t* out, void* stream) {
   if (mlb::page_bytes_of(f) == 0) return MLA_LB_EFORMAT;

@@ -55,6 +55,7 @@ def _load():
                                                 I32, I32, I32, I32, F, I32, P, SZ, P, P, P]),
         "mla_lb_channel_stat": (ctypes.c_int, [P, I64, I32, ctypes.c_double, P]),
         "mla_lb_smooth_scales": (ctypes.c_int, [P, I32, F, I32, P]),
+        "mla_lb_hadamard_rows": (ctypes.c_int, [P, I64, I32, P]),
         "mla_lb_dequant_dump": (ctypes.c_int, [ctypes.c_int, P, I64, I64, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -71,7 +72,7 @@ EXPORTED = ("mla_lb_version", "mla_lb_strerror", "mla_lb_page_bytes",
             "mla_lb_prot_bytes_per_seq", "kv_quant_append", "mla_decode_lowbit_workspace",
             "mla_decode_lowbit", "mla_decode_lowbit_append", "mla_decode_lowbit_mq_workspace",
             "mla_decode_lowbit_mq", "mla_lb_channel_stat", "mla_lb_smooth_scales",
-            "mla_lb_dequant_dump")
+            "mla_lb_hadamard_rows", "mla_lb_dequant_dump")
 
 
 def raw():
@@ -356,6 +357,19 @@ def mla_lb_smooth_scales(stat, alpha, pair_tied=False):
     _check("mla_lb_smooth_scales",
            _lib.mla_lb_smooth_scales(a.ctypes.data, a.shape[0], float(alpha), int(bool(pair_tied)),
                                      out.ctypes.data))
+    return out
+
+
+def mla_lb_hadamard_rows(x):
+    """Host helper: x (numpy float32 [rows, n], n a power of two) times the
+    normalized Hadamard matrix H_n; returns float32 [rows, n]."""
+    import numpy as np
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    if a.ndim != 2:
+        raise ValueError(f"x: shape {a.shape}, expected (rows, n)")
+    out = np.empty_like(a)
+    _check("mla_lb_hadamard_rows",
+           _lib.mla_lb_hadamard_rows(a.ctypes.data, a.shape[0], a.shape[1], out.ctypes.data))
     return out
 
 

@@ -304,6 +304,23 @@ int mla_lb_smooth_scales(const float* stat, int32_t n, float alpha, int32_t pair
                          float* scales);
 
 /*
+ * mla_lb_hadamard_rows -- y[r] = x[r] . H_n for r < rows (host, pure), with
+ * H_n the normalized Hadamard matrix of order n (Sylvester's +-1 matrix
+ * divided by sqrt(n); symmetric and orthogonal, so H_n is its own inverse).
+ * The content-path rotation [QuantMLA §3.1, App. C.1] in its fixed form, the
+ * deterministic normalized Hadamard of the QuaRot-style baseline
+ * [QuantMLA App. D.2]: the latent is cached as c.H (folded into the
+ * projection that produces it), the absorbed content query becomes q.H, and
+ * the aggregated latent o' maps back as o'.H -- attention is unchanged in
+ * exact arithmetic, and each token's outlier channels are spread over all
+ * groups before quantization.  Computed in fp64 (fast Walsh-Hadamard
+ * butterflies), rounded once to fp32.
+ *   x, y  host fp32 [rows][n] (may be the same buffer); n a power of two,
+ *   n <= 2^20; rows >= 1.
+ */
+int mla_lb_hadamard_rows(const float* x, int64_t rows, int32_t n, float* y);
+
+/*
  * mla_lb_dequant_dump -- write the bf16 rows the decode kernel reconstructs
  * for every slot of one page, [64][576] = [c^ | k^_R], using the same device
  * code as mla_decode_lowbit.  For checking the reconstruction bit for bit.

@@ -24,6 +24,18 @@ What is computed, and where it is stated:
   in every consumer: queries become q / s (scores unchanged) and the
   aggregated latent is divided by s (the value route).  The RoPE key is
   compensated in the query only.
+* Content path [QuantMLA §3.1, App. C.1]: the cache holds the latent in
+  rotated and scaled coordinates, c' = c R_C S_C (row vectors), with R_C
+  orthogonal and S_C = Diag(s_C) positive; every consumer of the latent is
+  compensated.  In the absorbed decode form that is q' = q R_C S_C^-1 for the
+  content query (so q' . c' = q R S^-1 S R^T c^T = q . c) and
+  o = o' S_C^-1 R_C^T for the aggregated latent (o' = sum_i p_i c'_i =
+  o R_C S_C).  Both keys and values come from the one shared latent, so the
+  one transformed cache serves the score and the aggregation.  The fixed
+  rotation taken here is the deterministic normalized Hadamard matrix of the
+  QuaRot-style baseline [QuantMLA App. D.2], H_n = Sylvester's +-1 matrix of
+  order n divided by sqrt(n); the learned Cayley-parameterised rotation of
+  the method itself needs training data and is out of reach.
 * Selection [QuantMLA App. D.2]: alpha is chosen from {0, 0.125, 0.25, 0.5,
   0.75, 1} by held-out normalized attention-output MSE, the content and RoPE
   caches calibrated separately with the other kept exact; a tie keeps the
@@ -131,3 +143,57 @@ def select_alpha(calib_c, calib_kr, heldout, fmt, scale, path):
         errs[al] = float(np.mean(e))
     best = min(ALPHAS, key=lambda al: (errs[al], al))
     return best, errs, smooth_scales(a, best, pairs=(path == "rope"))
+
+
+def hadamard(n):
+    """Normalized Hadamard matrix of order n (a power of two) by Sylvester's
+    doubling: H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]], then / sqrt(n).
+    Symmetric and orthogonal."""
+    if n < 1 or n & (n - 1):
+        raise ValueError("order must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h / np.sqrt(n)
+
+
+def rotate_inputs(c_bits, q_lat_bits, R, s_c=None):
+    """The content cache rows and content queries of the transformed model,
+    stored in bf16: c' = c R S, q' = q R S^-1 (S = Diag(s_c), identity when
+    s_c is None).  RoPE keys and queries are untouched."""
+    s_c = np.ones(quant.D_C) if s_c is None else np.asarray(s_c, np.float64)
+    c = quant.bf16_to_f32(c_bits).astype(np.float64) @ R * s_c
+    q = quant.bf16_to_f32(q_lat_bits).astype(np.float64) @ R / s_c
+    return quant.f32_to_bf16(c.astype(np.float32)), quant.f32_to_bf16(q.astype(np.float32))
+
+
+def unrotate_output(out, R, s_c=None):
+    """Aggregated latent back in the original coordinates: o = o' S^-1 R^T."""
+    s_c = np.ones(quant.D_C) if s_c is None else np.asarray(s_c, np.float64)
+    return (np.asarray(out, np.float64) / s_c) @ R.T
+
+
+def attend_rotated_exact(c, kr, q_lat, q_rope, scale, R, s_c=None):
+    """The transformed cache in exact arithmetic (fp64, no bf16 storage, no
+    quantization): attention over c' = c R S with queries q' = q R S^-1,
+    output mapped back.  Equals attention over c for orthogonal R."""
+    s_c = np.ones(quant.D_C) if s_c is None else np.asarray(s_c, np.float64)
+    c2 = np.asarray(c, np.float64) @ R * s_c
+    q2 = np.asarray(q_lat, np.float64) @ R / s_c
+    rows = np.concatenate([c2, np.asarray(kr, np.float64)], axis=1)
+    out, lse = attention.attend(q2, np.asarray(q_rope, np.float64), rows, scale)
+    return unrotate_output(out, R, s_c), lse
+
+
+def decode_rotated(c_bits, kr_bits, q_lat_bits, q_rope_bits, fmt, scale, R, s_c=None):
+    """Decode over the low-bit cache of the transformed model: the rotated
+    (and scaled) content rows are stored in bf16 and go through the format's
+    quantizer like any cache row (protected tokens keep their bf16 rows); the
+    output is mapped back to the original coordinates.
+
+    returns (out [H,512], lse [H]) float64."""
+    c2, q2 = rotate_inputs(c_bits, q_lat_bits, R, s_c)
+    rows = attention.effective_rows(c2, kr_bits, fmt)
+    out, lse = attention.attend(quant.bf16_to_f32(q2).astype(np.float64),
+                                quant.bf16_to_f32(q_rope_bits).astype(np.float64), rows, scale)
+    return unrotate_output(out, R, s_c), lse

@@ -141,6 +141,22 @@ int main() {
   CHECK(mla_lb_channel_stat(u16, 0, 4, 50.0, f32) == MLA_LB_ESHAPE);
   CHECK(mla_lb_smooth_scales(f32, 3, 0.5f, 1, f32) == MLA_LB_ESHAPE);
 
+  // Hadamard rows: H_n H_n = I (apply twice), and n = 2 by hand
+  for (int32_t nh : {1, 2, 8, 512}) {
+    std::vector<float> x(3 * nh), y(3 * nh), z(3 * nh);
+    for (size_t i = 0; i < x.size(); ++i) x[i] = static_cast<float>((i * 7919) % 113) - 56.0f;
+    CHECK(mla_lb_hadamard_rows(x.data(), 3, nh, y.data()) == MLA_LB_OK);
+    CHECK(mla_lb_hadamard_rows(y.data(), 3, nh, z.data()) == MLA_LB_OK);
+    for (size_t i = 0; i < x.size(); ++i) CHECK(std::fabs(z[i] - x[i]) <= 1e-4f);
+  }
+  {
+    float x2[2] = {3.0f, 1.0f}, y2[2];
+    CHECK(mla_lb_hadamard_rows(x2, 1, 2, y2) == MLA_LB_OK);
+    CHECK(std::fabs(y2[0] - 4.0f / std::sqrt(2.0f)) < 1e-6f && std::fabs(y2[1] - 2.0f / std::sqrt(2.0f)) < 1e-6f);
+    CHECK(mla_lb_hadamard_rows(x2, 1, 3, y2) == MLA_LB_ESHAPE);
+    CHECK(mla_lb_hadamard_rows(nullptr, 1, 2, y2) == MLA_LB_EINVAL);
+  }
+
   if (failures) std::fprintf(stderr, "%d checks failed\n", failures);
   else std::printf("abi host checks passed\n");
   return failures ? 1 : 0;

@@ -343,3 +343,18 @@ def test_host_layer_under_address_and_ub_sanitizers(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
     assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-4000:])
     assert "abi host checks passed" in r.stdout
+
+
+def test_hadamard_helper_matches_oracle(ops):
+    """mla_lb_hadamard_rows against the oracle's Sylvester matrix product
+    (fp64 reference, the helper rounds once to fp32); bad orders refused."""
+    import numpy as np
+    from oracle import transforms
+    rng = np.random.default_rng(3)
+    for n in (1, 2, 64, 512):
+        x = (rng.standard_normal((5, n)) * 10).astype(np.float32)
+        want = x.astype(np.float64) @ transforms.hadamard(n)
+        got = ops.mla_lb_hadamard_rows(x)
+        np.testing.assert_allclose(got, want, rtol=2e-7, atol=1e-6 * np.abs(want).max())
+    with pytest.raises(ops.MlaLowbitError):
+        ops.mla_lb_hadamard_rows(np.zeros((2, 48), np.float32))

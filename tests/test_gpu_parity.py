@@ -584,6 +584,50 @@ def test_calibrated_scales_through_kernels():
         assert e_sc < e_rtn / 3, (e_rtn, e_sc)
 
 
+@pytest.mark.parametrize("H", [16, 128])
+def test_hadamard_rotated_cache_through_kernels(H):
+    """The content-path rotation [QuantMLA §3.1, App. C.1] in its fixed
+    normalized-Hadamard form [QuantMLA App. D.2], applied with the library's
+    host helper as a model with the rotation folded into its projections
+    would produce the cache: latent rows and content queries times H, the
+    RoPE path unchanged.  The kernels run unchanged: the decode of the
+    rotated cache matches the oracle on the same inputs, and mapped back
+    (o' H) it is closer to full-precision attention than the decode of the
+    unrotated cache on x16 outlier channels."""
+    from bit_mla_kv_quant_amd import ops
+    from oracle import transforms
+    from test_oracle_transforms import _outlier_draw
+    d = _outlier_draw(seed=7, L=700, heads=H)
+    say("hadamard rotation", H)
+    plain = GpuCache(d)
+    plain.fill()
+    o_rtn, _ = plain.decode()
+
+    def rot_bf16(bits):
+        flat = quant.bf16_to_f32(bits).reshape(-1, 512)
+        return quant.f32_to_bf16(ops.mla_lb_hadamard_rows(flat)).reshape(np.shape(bits))
+    t = synth.small(fmt="C4R4", batch=3, heads=H, lens=tuple(d.lens), seed=7)
+    t.c = [rot_bf16(x) for x in d.c]
+    t.kr = d.kr
+    t.q_lat = rot_bf16(d.q_lat)
+    t.q_rope = d.q_rope
+    t.block_table, t.num_pages = d.block_table, d.num_pages
+    # the helper's rotation is the oracle's (inputs of both sides agree)
+    h = transforms.hadamard(512)
+    want_c, want_q = transforms.rotate_inputs(d.c[1], d.q_lat[1], h)
+    assert np.mean(t.c[1] != want_c) < 1e-3 and np.mean(t.q_lat[1] != want_q) < 1e-3
+    rot = GpuCache(t)
+    rot.fill()
+    o_rot, l_rot = rot.decode()
+    check_decode(t, rot, o_rot, l_rot, t.lens)           # parity on the rotated inputs
+    for b in (1, 2):
+        ref, _ = transforms.exact_decode(d.c[b], d.kr[b], d.q_lat[b], d.q_rope[b], d.scale)
+        back = ops.mla_lb_hadamard_rows(o_rot[b].astype(np.float32)).astype(np.float64)
+        e_rtn, e_rot = transforms.nmse(o_rtn[b], ref), transforms.nmse(back, ref)
+        say(f"  seq {b}: NMSE plain {e_rtn:.2e}, rotated {e_rot:.2e}")
+        assert e_rot < e_rtn / 3, (e_rtn, e_rot)
+
+
 # ------------------------------------------------------------ HIP graphs ---
 @pytest.mark.parametrize("H", [16, 128])
 def test_graph_replay_matches_eager(H):

@@ -109,3 +109,83 @@ def test_alpha_search_exact_tie_keeps_smallest_alpha(path):
         assert len(set(errs.values())) == 1, errs    # an exact tie
         assert al == min(order) == 0.0
         assert np.all(s == 1.0)
+
+
+# ------------------------------------------------- content-path rotation ---
+def test_hadamard_matrix_against_library_and_closed_form():
+    """Known answer H_2 = [[1, 1], [1, -1]] / sqrt(2); every order up to 512
+    equals scipy's Sylvester Hadamard matrix / sqrt(n); orthogonal and
+    symmetric."""
+    import scipy.linalg
+    np.testing.assert_array_equal(transforms.hadamard(2) * np.sqrt(2), [[1, 1], [1, -1]])
+    for n in (1, 2, 4, 8, 64, 512):
+        h = transforms.hadamard(n)
+        np.testing.assert_allclose(h, scipy.linalg.hadamard(n) / np.sqrt(n), rtol=0, atol=1e-15)
+        np.testing.assert_allclose(h @ h.T, np.eye(n), rtol=0, atol=1e-12)
+        np.testing.assert_array_equal(h, h.T)
+    with pytest.raises(ValueError):
+        transforms.hadamard(48)
+
+
+def _rotation_case(seed, L=300, H=8):
+    rng = np.random.default_rng(seed)
+    c = rng.standard_normal((L, 512)) * np.exp(0.5 * rng.standard_normal(512))
+    kr = rng.standard_normal((L, 64))
+    ql = rng.standard_normal((H, 512)) * 0.07
+    qr = rng.standard_normal((H, 64)) * 0.07
+    return c, kr, ql, qr
+
+
+def test_content_rotation_preserves_attention_exactly():
+    """[QuantMLA §3.1, App. C.1]: with every consumer compensated, an
+    orthogonal rotation (the normalized Hadamard, and a random orthogonal
+    matrix) times a positive channel scale leaves attention unchanged -- in
+    exact arithmetic the transformed decode equals the plain one to fp64
+    rounding, output and lse."""
+    from oracle import attention
+    rng = np.random.default_rng(11)
+    c, kr, ql, qr = _rotation_case(11)
+    rows = np.concatenate([c, kr], axis=1)
+    ref, rl = attention.attend(ql, qr, rows, 0.07)
+    Q, _ = np.linalg.qr(rng.standard_normal((512, 512)))
+    for R in (transforms.hadamard(512), Q):
+        for s_c in (None, np.exp(rng.uniform(-2, 2, 512))):
+            out, lse = transforms.attend_rotated_exact(c, kr, ql, qr, 0.07, R, s_c)
+            np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(lse, rl, rtol=1e-12, atol=1e-12)
+
+
+def test_content_rotation_negative_control_non_orthogonal():
+    """A matrix that is not orthogonal (the Hadamard with one column scaled by
+    1.1, or perturbed by 1e-2) does not preserve attention: the identity above
+    is the orthogonality, not the bookkeeping."""
+    from oracle import attention
+    rng = np.random.default_rng(12)
+    c, kr, ql, qr = _rotation_case(12)
+    ref, _ = attention.attend(ql, qr, np.concatenate([c, kr], axis=1), 0.07)
+    h = transforms.hadamard(512)
+    bad1 = h.copy()
+    bad1[:, 0] *= 1.1
+    bad2 = h + 1e-2 * rng.standard_normal((512, 512))
+    for R in (bad1, bad2):
+        out, _ = transforms.attend_rotated_exact(c, kr, ql, qr, 0.07, R)
+        assert transforms.nmse(out, ref) > 1e-6
+
+
+def test_hadamard_rotation_lowers_int4_error_on_outlier_channels():
+    """On a cache with x16 outlier content channels, the normalized Hadamard
+    spreads each token's outliers over all 512 channels, so every 64-group
+    has a smaller range and the INT4 attention-output NMSE (against exact
+    attention over the original bf16 cache) drops well below plain
+    round-to-nearest on the original coordinates."""
+    from oracle import attention
+    d = _outlier_draw(seed=7, L=700)
+    h = transforms.hadamard(512)
+    for b in (1, 2):
+        ref, _ = transforms.exact_decode(d.c[b], d.kr[b], d.q_lat[b], d.q_rope[b], d.scale)
+        o_rtn, _ = attention.decode_sequence(d.c[b], d.kr[b], d.q_lat[b], d.q_rope[b], "C4R4",
+                                             d.scale)
+        o_rot, _ = transforms.decode_rotated(d.c[b], d.kr[b], d.q_lat[b], d.q_rope[b], "C4R4",
+                                             d.scale, h)
+        e_rtn, e_rot = transforms.nmse(o_rtn, ref), transforms.nmse(o_rot, ref)
+        assert e_rot < e_rtn / 3, (b, e_rtn, e_rot)
