@@ -34,6 +34,7 @@ UNITS = {
     # the 16-row kernel is VALU-bound with two waves per SIMD: the ILP-first
     # scheduler (242-244 VGPRs, still two waves) took 0.8 % off its calls
     "decode_h16.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"],
+    "noalloc.hip": [],
     "abi.cpp": ["-x", "hip"],
 }
 

@@ -51,7 +51,7 @@ static int device_cu_count() {
 // shorter than a minimum number of pages (each split costs a heads x 512 fp32
 // partial write).  Head blocks are 128 rows when use_rows128(H), else 16.
 
-Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits) {
+Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits, size_t ws_cap) {
   Plan p{1, 1, 0};
   const int64_t P = (static_cast<int64_t>(max_seq_len) + 63) / 64;
   if (P <= 1) return p;
@@ -64,6 +64,12 @@ Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits) {
     ns = (static_cast<int64_t>(device_cu_count()) * kWavesTarget + groups - 1) / groups;
     const int64_t cap = P / (h128 ? kMinPagesPerSplit128 : kMinPagesPerSplit);
     if (ns > cap) ns = cap;
+    if (ws_cap > 0) {              // no more splits than a workspace of ws_cap bytes holds
+      const uint64_t per_split = static_cast<uint64_t>(B) * static_cast<uint64_t>(H) *
+                                 (512 + 4) * sizeof(float);
+      const int64_t fit = static_cast<int64_t>(ws_cap / per_split);
+      if (ns > fit) ns = fit < 2 ? 1 : fit;
+    }
   }
   if (ns < 1) ns = 1;
   if (ns > P) ns = P;
@@ -131,17 +137,20 @@ int mla_decode_lowbit_workspace(int f, int32_t B, int32_t H, int32_t max_seq_len
 
 }  // extern "C"
 
-namespace {
+namespace mlb {
 
-// Validation and dispatch shared by the decode entry points.  new_c / new_r
-// non-null selects the fused writer (pages / prot are then written).
-int decode_entry(int f, const uint16_t* q_lat, const uint16_t* q_rope, const uint8_t* pages,
+// Validation and split plan shared by the decode entry points: host code
+// only, no HIP call.  Fills every field of `a` except the workspace
+// pointers (set_workspace).  new_c / new_r non-null selects the fused writer
+// (pages / prot are then written).  ws_cap > 0 limits the automatic plan to
+// that many workspace bytes.
+int decode_setup(int f, const uint16_t* q_lat, const uint16_t* q_rope, const uint8_t* pages,
                  int64_t num_pages, const uint16_t* prot, int32_t num_seq_slots,
                  const int32_t* seq_slot, const int32_t* block_table, int32_t max_blocks,
                  const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t H,
-                 float softmax_scale, int32_t num_splits, void* workspace,
-                 size_t workspace_bytes, float* out, float* lse, void* stream,
-                 const uint16_t* new_c, const uint16_t* new_r, int32_t nq = 1) {
+                 float softmax_scale, int32_t num_splits, float* out, float* lse,
+                 const uint16_t* new_c, const uint16_t* new_r, int32_t nq, size_t ws_cap,
+                 DecodeArgs& a, Plan& plan) {
   if (mlb::page_bytes_of(f) == 0) return MLA_LB_EFORMAT;
   if (!q_lat || !q_rope || !pages || !prot || !seq_slot || !block_table || !seq_lens || !out ||
       !lse)
@@ -156,12 +165,8 @@ int decode_entry(int f, const uint16_t* q_lat, const uint16_t* q_rope, const uin
   if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks) * 64)
     return MLA_LB_ESHAPE;
   if (B > 65535) return MLA_LB_ESHAPE;               // grid.y limit
-  const mlb::Plan plan = mlb::make_plan(B, H, max_seq_len, num_splits);
-  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
-    return MLA_LB_EWORKSPACE;
-  float* ws = static_cast<float*>(workspace);
-  const size_t n_o = static_cast<size_t>(B) * plan.nsplit * H * 512;
-  mlb::DecodeArgs a{};
+  plan = mlb::make_plan(B, H, max_seq_len, num_splits, ws_cap);
+  a = mlb::DecodeArgs{};
   a.q_lat = q_lat;
   a.q_rope = q_rope;
   a.pages = pages;
@@ -180,14 +185,45 @@ int decode_entry(int f, const uint16_t* q_lat, const uint16_t* q_rope, const uin
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.pps = plan.pps;
   a.nsplit = plan.nsplit;
-  a.ws_o = plan.nsplit > 1 ? ws : nullptr;
-  a.ws_ml = plan.nsplit > 1 ? ws + n_o : nullptr;
   a.out = out;
   a.lse = lse;
   a.new_c = new_c;
   a.new_r = new_r;
   a.wpages = const_cast<uint8_t*>(pages);
   a.wprot = const_cast<uint16_t*>(prot);
+  return MLA_LB_OK;
+}
+
+// Workspace layout: [B][nsplit][H][512] partial outputs, then [B][nsplit][H][4].
+void set_workspace(DecodeArgs& a, const Plan& plan, void* workspace) {
+  float* ws = static_cast<float*>(workspace);
+  const size_t n_o = static_cast<size_t>(a.B) * plan.nsplit * a.H * 512;
+  a.ws_o = plan.nsplit > 1 ? ws : nullptr;
+  a.ws_ml = plan.nsplit > 1 ? ws + n_o : nullptr;
+}
+
+}  // namespace mlb
+
+namespace {
+
+// The decode entry points with a caller-supplied workspace.
+int decode_entry(int f, const uint16_t* q_lat, const uint16_t* q_rope, const uint8_t* pages,
+                 int64_t num_pages, const uint16_t* prot, int32_t num_seq_slots,
+                 const int32_t* seq_slot, const int32_t* block_table, int32_t max_blocks,
+                 const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t H,
+                 float softmax_scale, int32_t num_splits, void* workspace,
+                 size_t workspace_bytes, float* out, float* lse, void* stream,
+                 const uint16_t* new_c, const uint16_t* new_r, int32_t nq = 1) {
+  mlb::DecodeArgs a;
+  mlb::Plan plan;
+  const int rc = mlb::decode_setup(f, q_lat, q_rope, pages, num_pages, prot, num_seq_slots,
+                                   seq_slot, block_table, max_blocks, seq_lens, max_seq_len, B, H,
+                                   softmax_scale, num_splits, out, lse, new_c, new_r, nq, 0, a,
+                                   plan);
+  if (rc != MLA_LB_OK) return rc;
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return MLA_LB_EWORKSPACE;
+  mlb::set_workspace(a, plan, workspace);
   return mlb::launch_decode(f, a, static_cast<hipStream_t>(stream));
 }
 

@@ -71,7 +71,21 @@ struct Plan {
   size_t ws_bytes;   // workspace needed (0 when nsplit == 1)
 };
 
-Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits);
+// ws_cap > 0: the automatic plan (num_splits == 0) takes no more splits than
+// a workspace of ws_cap bytes holds (a single split when not even two fit).
+Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits,
+               size_t ws_cap = 0);
+
+// Host-side validation and plan of a decode call (no HIP call), and the
+// workspace pointers of the plan; both in abi.cpp.
+int decode_setup(int f, const uint16_t* q_lat, const uint16_t* q_rope, const uint8_t* pages,
+                 int64_t num_pages, const uint16_t* prot, int32_t num_seq_slots,
+                 const int32_t* seq_slot, const int32_t* block_table, int32_t max_blocks,
+                 const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t H,
+                 float softmax_scale, int32_t num_splits, float* out, float* lse,
+                 const uint16_t* new_c, const uint16_t* new_r, int32_t nq, size_t ws_cap,
+                 DecodeArgs& a, Plan& plan);
+void set_workspace(DecodeArgs& a, const Plan& plan, void* workspace);
 
 int launch_append(int f, const AppendArgs& a, hipStream_t stream);
 int launch_decode(int f, const DecodeArgs& a, hipStream_t stream);

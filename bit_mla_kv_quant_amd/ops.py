@@ -49,6 +49,8 @@ def _load():
         "mla_decode_lowbit_append": (ctypes.c_int, [ctypes.c_int, P, P, P, P, P, I64, P, I32, P,
                                                     P, I32, P, I32, I32, I32, F, I32, P, SZ, P,
                                                     P, P]),
+        "mla_decode_lowbit_noalloc": (ctypes.c_int, [ctypes.c_int, P, P, P, I64, P, I32, P, P,
+                                                     I32, P, I32, I32, I32, F, I32, P, P, P]),
         "mla_decode_lowbit_mq_workspace": (ctypes.c_int, [ctypes.c_int, I32, I32, I32, I32, I32,
                                                           ctypes.POINTER(SZ)]),
         "mla_decode_lowbit_mq": (ctypes.c_int, [ctypes.c_int, P, P, P, I64, P, I32, P, P, I32, P,
@@ -70,7 +72,8 @@ _lib = _load()
 # Names the header declares (checked by the ABI tests).
 EXPORTED = ("mla_lb_version", "mla_lb_strerror", "mla_lb_page_bytes",
             "mla_lb_prot_bytes_per_seq", "kv_quant_append", "mla_decode_lowbit_workspace",
-            "mla_decode_lowbit", "mla_decode_lowbit_append", "mla_decode_lowbit_mq_workspace",
+            "mla_decode_lowbit", "mla_decode_lowbit_append", "mla_decode_lowbit_noalloc",
+            "mla_decode_lowbit_mq_workspace",
             "mla_decode_lowbit_mq", "mla_lb_channel_stat", "mla_lb_smooth_scales",
             "mla_lb_hadamard_rows", "mla_lb_dequant_dump")
 
@@ -250,6 +253,40 @@ def mla_decode_lowbit(fmt, q_lat, q_rope, pages, prot, seq_slot, block_table, se
         None if workspace is None else ctypes.c_void_p(workspace.data_ptr()), ws_bytes,
         _ptr(out, (torch.float32,), "out"), _ptr(lse, (torch.float32,), "lse"), _stream(stream))
     _check("mla_decode_lowbit", code)
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def mla_decode_lowbit_noalloc(fmt, q_lat, q_rope, pages, prot, seq_slot, block_table, seq_lens,
+                              max_seq_len, softmax_scale, num_splits=0, out=None, lse=None,
+                              stream=None):
+    """mla_decode_lowbit with the split partials in the library's per-GPU
+    scratch (no workspace, no allocation by the call); out / lse are
+    allocated here only when not passed.  Returns (out, lse)."""
+    if q_lat.dim() != 3:
+        raise ValueError(f"q_lat: shape {tuple(q_lat.shape)}, expected (B, H, 512)")
+    B, H = q_lat.shape[0], q_lat.shape[1]
+    _decode_shapes(fmt, q_lat, q_rope, pages, prot, seq_slot, block_table, seq_lens, out, lse,
+                   (B, H))
+    _same_gpu("mla_decode_lowbit_noalloc", ("q_lat", q_lat), ("q_rope", q_rope),
+              ("pages", pages), ("prot", prot), ("seq_slot", seq_slot),
+              ("block_table", block_table), ("seq_lens", seq_lens), ("out", out), ("lse", lse))
+    dev = q_lat.device
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    code = _lib.mla_decode_lowbit_noalloc(
+        _fmt(fmt), _ptr(q_lat, _BF16, "q_lat"), _ptr(q_rope, _BF16, "q_rope"),
+        _ptr(pages, (torch.uint8,), "pages"), pages.shape[0], _ptr(prot, _BF16, "prot"),
+        prot.shape[0], _ptr(seq_slot, (torch.int32,), "seq_slot"),
+        _ptr(block_table, (torch.int32,), "block_table"), block_table.shape[1],
+        _ptr(seq_lens, (torch.int32,), "seq_lens"), int(max_seq_len), B, H,
+        float(softmax_scale), int(num_splits),
+        _ptr(out, (torch.float32,), "out"), _ptr(lse, (torch.float32,), "lse"), _stream(stream))
+    _check("mla_decode_lowbit_noalloc", code)
     return out, lse
 
 

@@ -95,7 +95,8 @@ enum {
   MLA_LB_PAGE_TOKENS = 64, /* tokens per page       [QuantMLA App. C.5] */
   MLA_LB_PROT_ROWS = 132,  /* 4 sink + 128 recent   [QuantMLA App. C.5] */
   MLA_LB_MAX_HEADS = 128,
-  MLA_LB_MAX_ROWS = 1024   /* queries x heads per sequence (mla_decode_lowbit_mq) */
+  MLA_LB_MAX_ROWS = 1024,  /* queries x heads per sequence (mla_decode_lowbit_mq) */
+  MLA_LB_NOALLOC_SCRATCH_BYTES = 64 << 20  /* per-GPU scratch of mla_decode_lowbit_noalloc */
 };
 
 /* Library ABI version (host, pure). */
@@ -235,6 +236,36 @@ int mla_decode_lowbit_append(int f, const uint16_t* latent, const uint16_t* k_ro
                              int32_t B, int32_t H, float softmax_scale, int32_t num_splits,
                              void* workspace, size_t workspace_bytes, float* out, float* lse,
                              void* stream);
+
+/*
+ * mla_decode_lowbit_noalloc -- mla_decode_lowbit for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument, and no
+ * allocation by the call.  The split partials go to a scratch array of
+ * MLA_LB_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on each GPU
+ * it runs on until the process ends.
+ *   - Same arguments, result and errors as mla_decode_lowbit, without
+ *     workspace / workspace_bytes.
+ *   - num_splits = 0: the automatic plan, limited to as many splits as the
+ *     scratch holds (B * splits * H * 516 * 4 bytes <= 64 MiB; one split,
+ *     which needs no scratch, when not even two fit).  With the same plan the
+ *     result is bit-identical to mla_decode_lowbit's.
+ *   - num_splits > 0 whose partials exceed the scratch: MLA_LB_EWORKSPACE,
+ *     returned on the host before any HIP call.
+ *   - The first call on a device looks up that device's scratch address
+ *     (hipGetSymbolAddress, a host call that allocates nothing); make it
+ *     outside a graph capture.  A failed lookup returns MLA_LB_EHIP.
+ *   - Calls on one GPU share its scratch: calls that overlap in time on one
+ *     GPU (different streams or host threads) race and give undefined
+ *     results.  Serialise them (one stream, or events).
+ */
+int mla_decode_lowbit_noalloc(int f, const uint16_t* q_lat, const uint16_t* q_rope,
+                              const uint8_t* pages, int64_t num_pages, const uint16_t* prot,
+                              int32_t num_seq_slots, const int32_t* seq_slot,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t H,
+                              float softmax_scale, int32_t num_splits, float* out, float* lse,
+                              void* stream);
 
 /*
  * mla_decode_lowbit_mq_workspace -- bytes of workspace mla_decode_lowbit_mq

@@ -117,6 +117,31 @@ int main() {
   CHECK(mla_lb_dequant_dump(0, u8, 10, 10, u16, nullptr) == MLA_LB_ESHAPE);
   CHECK(mla_lb_dequant_dump(0, u8, 10, 9, u16, nullptr) == MLA_LB_OK);
 
+  // no-alloc variant: validation and plan limits on the host, before any HIP
+  // call (the scratch lookup needs a device; a single-split plan needs none)
+  {
+    const size_t cap = MLA_LB_NOALLOC_SCRATCH_BYTES;
+    const int32_t B = 64, H = 128, L = 2500, mb = (L + 63) / 64;
+    const size_t per_split = static_cast<size_t>(B) * H * 516 * 4;
+    const mlb::Plan capped = mlb::make_plan(B, H, L, 0, cap);
+    const mlb::Plan full = mlb::make_plan(B, H, L, 0);
+    CHECK(capped.ws_bytes <= cap && capped.nsplit >= 1);
+    CHECK(full.ws_bytes <= cap || capped.nsplit == static_cast<int32_t>(cap / per_split));
+    CHECK(mlb::make_plan(1, 16, 100000, 0, cap).nsplit == mlb::make_plan(1, 16, 100000, 0).nsplit);
+    CHECK(mlb::make_plan(65535, 128, 100000, 0, cap).nsplit == 1);   // not even two fit
+    const int32_t too_many = static_cast<int32_t>(cap / per_split) + 1;
+    CHECK(mla_decode_lowbit_noalloc(0, u16, u16, u8, 10, u16, 1, i32, i32, mb, i32, L, B, H, 0.1f,
+                                    too_many, f32, f32, nullptr) == MLA_LB_EWORKSPACE);
+    CHECK(mla_decode_lowbit_noalloc(0, nullptr, u16, u8, 10, u16, 1, i32, i32, mb, i32, L, B, H,
+                                    0.1f, 0, f32, f32, nullptr) == MLA_LB_EINVAL);
+    CHECK(mla_decode_lowbit_noalloc(7, u16, u16, u8, 10, u16, 1, i32, i32, mb, i32, L, B, H, 0.1f,
+                                    0, f32, f32, nullptr) == MLA_LB_EFORMAT);
+    const int before = mlb::g_launches;
+    CHECK(mla_decode_lowbit_noalloc(0, u16, u16, u8, 10, u16, 1, i32, i32, mb, i32, L, B, H, 0.1f,
+                                    1, f32, f32, nullptr) == MLA_LB_OK);
+    CHECK(mlb::g_launches == before + 1 && mlb::g_last.nsplit == 1 && mlb::g_last.ws_o == nullptr);
+  }
+
   // calibration helpers on odd sizes, against a direct computation
   for (int64_t rows : {1, 2, 7, 1000})
     for (int32_t cols : {1, 3, 64}) {

@@ -321,7 +321,8 @@ def test_binding_requires_gpu_tensors(ops):
 
 
 def test_host_layer_under_address_and_ub_sanitizers(tmp_path):
-    """abi.cpp (validation, split plan, workspace sizing, calibration helpers)
+    """abi.cpp and noalloc.hip (validation, split plan, workspace sizing, the
+    no-alloc variant's plan limit, calibration helpers)
     built for the host with AddressSanitizer and UndefinedBehaviorSanitizer,
     the kernel launchers replaced by stubs, and driven through every host
     path by tests/native/abi_host_check.cpp; any memory error, leak or
@@ -333,6 +334,7 @@ def test_host_layer_under_address_and_ub_sanitizers(tmp_path):
            "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
            "-Xarch_host", "-fno-sanitize-recover=all",
            os.path.join(ROOT, "bit_mla_kv_quant_amd", "csrc", "abi.cpp"),
+           os.path.join(ROOT, "bit_mla_kv_quant_amd", "csrc", "noalloc.hip"),
            os.path.join(ROOT, "tests", "native", "abi_host_check.cpp"), "-o", str(exe)]
     if not os.path.exists(cmd[0]):
         pytest.skip("hipcc not available")
