@@ -244,10 +244,17 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
       const uint16_t* ka = kb + (32 * c + l32) * KT_PITCH + 8 * h;
+      // K slices are read SPF slices ahead of their MFMA (LDS latency)
+      constexpr int SPF = 4;
+      bf16x8 kn[SPF];
 #pragma unroll
-      for (int s = 0; s < 36; ++s)
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(ka + 16 * s), qv[s], sacc,
-                                                        0, 0, 0);
+      for (int s = 0; s < SPF; ++s) kn[s] = *(const bf16x8*)(ka + 16 * s);
+#pragma unroll
+      for (int s = 0; s < 36; ++s) {
+        const bf16x8 kv = kn[s % SPF];
+        if (s + SPF < 36) kn[s % SPF] = *(const bf16x8*)(ka + 16 * (s + SPF));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qv[s], sacc, 0, 0, 0);
+      }
       const int i_base = (p0 + k) * PAGE + 32 * c + 4 * h;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
