@@ -75,6 +75,47 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
+// Physical page ids of one split's pages, read from the block table through
+// vector loads into a window held one entry per lane: lane j of `cur` holds
+// split page w0 + j, lane j of `nxt` split page w0 + 64 + j, and `nxt` is
+// requested as soon as `cur` comes into use, 64 pages ahead of its first
+// read.  Entries come out of the window with readlane, so no scalar load (and
+// no wait on the counter LDS reads share) sits in a page loop.  Ids outside
+// [0, num_pages), and pages past the split, read as -1.  Callers ask for
+// page indices that never decrease (advance() before each new maximum) and
+// stay below w0 + 128.
+struct PageWindow {
+  const int32_t* row;   // block-table entries of the split's first page
+  int np;               // pages in the split
+  int64_t num_pages;
+  int w0;
+  int cur, nxt;
+
+  __device__ __forceinline__ int fetch(int k, int lane) const {
+    const int i = k + lane;
+    int v = -1;
+    if (i < np) v = row[i];
+    return (v >= 0 && v < num_pages) ? v : -1;
+  }
+  __device__ __forceinline__ void init(int lane) {
+    w0 = 0;
+    cur = fetch(0, lane);
+    nxt = fetch(64, lane);
+  }
+  // make page k (k >= w0) readable
+  __device__ __forceinline__ void advance(int k, int lane) {
+    if (k >= w0 + 64) {
+      w0 += 64;
+      cur = nxt;
+      nxt = fetch(w0 + 64, lane);
+    }
+  }
+  __device__ __forceinline__ int id(int k) const {
+    const int j = k - w0;
+    return j < 64 ? __builtin_amdgcn_readlane(cur, j) : __builtin_amdgcn_readlane(nxt, j - 64);
+  }
+};
+
 template <typename T, typename S>
 __device__ __forceinline__ T bitcast(const S& s) {
   static_assert(sizeof(T) == sizeof(S), "size");

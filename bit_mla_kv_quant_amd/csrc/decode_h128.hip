@@ -121,13 +121,8 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
     fused_store<F>(a, fused_load(a, b, wv, 4, lane), b, L, sq, wv, 4, lane);
   }
 
-  const __attribute__((address_space(4))) int32_t* bt_row =
-      (const __attribute__((address_space(4))) int32_t*)(a.block_table +
-                                                         (int64_t)b * a.max_blocks + p0);
-  auto page_id = [&](int k) -> int {              // -1 = unusable table entry
-    const int phys = bt_row[k];
-    return (phys >= 0 && phys < a.num_pages) ? phys : -1;
-  };
+  // physical page ids of the split (-1 = unusable table entry)
+  PageWindow pw{a.block_table + (int64_t)b * a.max_blocks + p0, np, a.num_pages, 0, 0, 0};
   auto page_ptr = [&](int phys) -> const uint8_t* {
     return a.pages + (int64_t)(phys >= 0 ? phys : 0) * Fmt<F>::PAGE_BYTES;
   };
@@ -314,13 +309,15 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
       for (int r = 0; r < 16; ++r) acc[nt][r] = 0.f;
     f_run = 0.f;
     if (threadIdx.x == 0) redo_flag = 0;
-    int id_k = page_id(0), id_k1 = page_id(min(1, np - 1));
+    pw.init(lane);
+    int id_k = pw.id(0), id_k1 = pw.id(min(1, np - 1));
     LaneSlot<F> cur = load_lane_slot<F>(page_ptr(id_k), tt, g);
     build_page(cur, 0, id_k);
     cur = load_lane_slot<F>(page_ptr(id_k1), tt, g);
     __syncthreads();
     for (int k = 0; k < np; ++k) {
-      const int id_k2 = page_id(min(k + 2, np - 1));
+      pw.advance(min(k + 2, np - 1), lane);
+      const int id_k2 = pw.id(min(k + 2, np - 1));
       if (k + 1 < np) {
         build_page(cur, k + 1, id_k1);
         cur = load_lane_slot<F>(page_ptr(id_k2), tt, g);

@@ -119,13 +119,8 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
   FusedRow fresh_row{};
   if (writer) fresh_row = fused_load(a, b, wave, NW, lane);
 
-  const __attribute__((address_space(4))) int32_t* bt_row =
-      (const __attribute__((address_space(4))) int32_t*)(a.block_table +
-                                                         (int64_t)b * a.max_blocks + p0);
-  auto page_id = [&](int k) -> int {              // -1 = unusable table entry
-    const int phys = bt_row[k];
-    return (phys >= 0 && phys < a.num_pages) ? phys : -1;
-  };
+  // physical page ids of the split (-1 = unusable table entry)
+  PageWindow pw{a.block_table + (int64_t)b * a.max_blocks + p0, p1 - p0, a.num_pages, 0, 0, 0};
   auto page_ptr = [&](int phys) -> const uint8_t* {
     return a.pages + (int64_t)(phys >= 0 ? phys : 0) * Fmt<F>::PAGE_BYTES;
   };
@@ -337,7 +332,7 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
   };
 
   auto load_quarter = [&](const int q) -> LaneSlot<F> {
-    return load_lane_slot<F>(page_ptr(page_id(q >> 2)), QT * (q & 3) + n16, g);
+    return load_lane_slot<F>(page_ptr(pw.id(q >> 2)), QT * (q & 3) + n16, g);
   };
 
   // ---- this wave's quarters wave, wave+8, ...; the codes of the next one
@@ -347,6 +342,7 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
 #pragma unroll
     for (int nb = 0; nb < 32; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     f_run = 0.f;
+    pw.init(lane);
     if (wave < nquart) {
       LaneSlot<F> cur = load_quarter(wave);
       for (int q = wave; q < nquart; q += NW) {
@@ -354,7 +350,8 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
         // neither finishes its quarters far ahead of the other
         if (((q >> 3) ^ (wave >> 2)) & 1) __builtin_amdgcn_s_setprio(1);
         else __builtin_amdgcn_s_setprio(0);
-        const int phys = page_id(q >> 2);
+        const int phys = pw.id(q >> 2);
+        pw.advance((q + NW < nquart ? q + NW : q) >> 2, lane);
         const f32x4 sc = ordinary(q, phys, cur) ? quarter(std::true_type{}, q, phys, cur)
                                                 : quarter(std::false_type{}, q, phys, cur);
         cur = load_quarter(q + NW < nquart ? q + NW : q);

@@ -214,6 +214,29 @@ __device__ __forceinline__ LaneSlot<F> load_lane_slot(const uint8_t* pg, int tt,
   return p;
 }
 
+// One half of load_lane_slot: PART 0 loads content group 2g (the first 64
+// of the lane's 128 content dims), both content groups' metadata and the
+// RoPE codes and metadata; PART 1 loads content group 2g+1.  Other fields of
+// p are left as they are.
+template <int F, int PART>
+__device__ __forceinline__ void load_lane_slot_half(LaneSlot<F>& p, const uint8_t* pg, int tt,
+                                                    int g) {
+  using FM = Fmt<F>;
+  if constexpr (FM::CBITS == 4) {
+    const uint8_t* row = pg + (g * PAGE + tt) * 64 + 32 * PART;
+    p.c[2 * PART] = *(const u32x4*)row;
+    p.c[2 * PART + 1] = *(const u32x4*)(row + 16);
+  } else {
+    p.c[PART] = *(const u32x4*)(pg + ((g >> 1) * PAGE + tt) * 64 + 32 * (g & 1) + 16 * PART);
+  }
+  if constexpr (PART == 0) {
+    p.r = *(const u32x2*)(pg + FM::OFF_R + tt * 32 + 8 * g);
+    p.mc = *(const u32x2*)(pg + FM::OFF_MC + tt * 32 + 8 * g);
+    if constexpr (FM::F32R) p.mr = *(const u32x2*)(pg + FM::OFF_MR + tt * 8);
+    else p.mr = *(const uint32_t*)(pg + FM::OFF_MR + tt * 4);
+  }
+}
+
 // (scale, zero) of a group: a bf16 pair in one word, or fp32 bit patterns
 __device__ __forceinline__ float meta_scale(uint32_t m) { return bf16_bits_to_f32(m & 0xffffu); }
 __device__ __forceinline__ float meta_zero(uint32_t m) { return bf16_bits_to_f32(m >> 16); }

@@ -13,7 +13,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmla_lowbit.so")
+# the in-tree build; MLA_LOWBIT_LIB names another build of the same library
+LIB_PATH = os.environ.get("MLA_LOWBIT_LIB") or os.path.join(_HERE, "libmla_lowbit.so")
 
 FORMATS = {"C4R4": 0, "C2R4": 1, "C4R4F": 2}
 
