@@ -52,7 +52,7 @@ static int device_cu_count() {
 // partial write).  Head blocks are 128 rows when use_rows128(H), else 16.
 
 Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits, size_t ws_cap) {
-  Plan p{1, 1, 0};
+  Plan p{1, 1, 0, false};
   const int64_t P = (static_cast<int64_t>(max_seq_len) + 63) / 64;
   if (P <= 1) return p;
   int64_t ns;
@@ -77,11 +77,15 @@ Plan make_plan(int32_t B, int32_t H, int32_t max_seq_len, int32_t num_splits, si
   ns = (P + pps - 1) / pps;
   p.pps = static_cast<int32_t>(pps);
   p.nsplit = static_cast<int32_t>(ns);
-  // B x nsplit x rows x (512 + 4) fp32: within the entry points' bounds
-  // (B <= 65535, nsplit <= 2^25 pages, rows <= 1024) below 2^63
-  if (ns > 1)
-    p.ws_bytes = static_cast<size_t>(B) * static_cast<size_t>(ns) * static_cast<size_t>(H) *
-                 (512 + 4) * sizeof(float);
+  // B x nsplit x rows x (512 + 4) fp32; within the entry points' bounds
+  // (B <= 65535, nsplit <= 2^25 pages, rows <= 65536) it can pass 2^64, so
+  // it is formed in 128 bits and a plan beyond 2^60 bytes is refused
+  if (ns > 1) {
+    const unsigned __int128 ws = static_cast<unsigned __int128>(B) * static_cast<uint64_t>(ns) *
+                                 static_cast<uint64_t>(H) * ((512 + 4) * sizeof(float));
+    if (ws > (static_cast<unsigned __int128>(1) << 60)) p.too_large = true;
+    else p.ws_bytes = static_cast<size_t>(ws);
+  }
   return p;
 }
 
@@ -131,7 +135,9 @@ int mla_decode_lowbit_workspace(int f, int32_t B, int32_t H, int32_t max_seq_len
       num_splits < 0)
     return MLA_LB_ESHAPE;
   if (B > 65535) return MLA_LB_ESHAPE;               // as the decode call
-  *bytes = mlb::make_plan(B, H, max_seq_len, num_splits).ws_bytes;
+  const mlb::Plan plan = mlb::make_plan(B, H, max_seq_len, num_splits);
+  if (plan.too_large) return MLA_LB_ESHAPE;
+  *bytes = plan.ws_bytes;
   return MLA_LB_OK;
 }
 
@@ -166,6 +172,7 @@ int decode_setup(int f, const uint16_t* q_lat, const uint16_t* q_rope, const uin
     return MLA_LB_ESHAPE;
   if (B > 65535) return MLA_LB_ESHAPE;               // grid.y limit
   plan = mlb::make_plan(B, H, max_seq_len, num_splits, ws_cap);
+  if (plan.too_large) return MLA_LB_ESHAPE;
   a = mlb::DecodeArgs{};
   a.q_lat = q_lat;
   a.q_rope = q_rope;
@@ -265,7 +272,9 @@ int mla_decode_lowbit_mq_workspace(int f, int32_t B, int32_t nq, int32_t H,
       static_cast<int64_t>(nq) * H > MLA_LB_MAX_ROWS || max_seq_len < 0 || num_splits < 0)
     return MLA_LB_ESHAPE;
   if (B > 65535) return MLA_LB_ESHAPE;               // as the decode call
-  *bytes = mlb::make_plan(B, nq * H, max_seq_len, num_splits).ws_bytes;
+  const mlb::Plan plan = mlb::make_plan(B, nq * H, max_seq_len, num_splits);
+  if (plan.too_large) return MLA_LB_ESHAPE;
+  *bytes = plan.ws_bytes;
   return MLA_LB_OK;
 }
 

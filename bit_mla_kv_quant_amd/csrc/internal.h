@@ -69,6 +69,7 @@ struct Plan {
   int32_t pps;       // pages per split (>= 1)
   int32_t nsplit;    // number of splits of a max-length sequence (>= 1)
   size_t ws_bytes;   // workspace needed (0 when nsplit == 1)
+  bool too_large;    // the workspace would pass 2^60 bytes: the call is refused
 };
 
 // ws_cap > 0: the automatic plan (num_splits == 0) takes no more splits than

@@ -70,6 +70,10 @@ WORKLOADS = {
     # (a speculative-decoding verify step or a chunked-prefill tail)
     6: Workload("v2lite_c4r4_b32_h16_l8k_q8", "C4R4", 32, 16, 8192, 8192, seed=20266,
                 queries=8),
+    # a chunked-prefill step on the V2 shape: 256 new tokens per sequence,
+    # each asking a query over its causal prefix of a 16K context
+    7: Workload("v2_c4r4_b4_h128_l16k_chunk256", "C4R4", 4, 128, 16384, 16384, seed=20267,
+                queries=256),
 }
 
 SOFTMAX_SCALE = 1.0 / math.sqrt(192.0)

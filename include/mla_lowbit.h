@@ -95,7 +95,8 @@ enum {
   MLA_LB_PAGE_TOKENS = 64, /* tokens per page       [QuantMLA App. C.5] */
   MLA_LB_PROT_ROWS = 132,  /* 4 sink + 128 recent   [QuantMLA App. C.5] */
   MLA_LB_MAX_HEADS = 128,
-  MLA_LB_MAX_ROWS = 1024,  /* queries x heads per sequence (mla_decode_lowbit_mq) */
+  MLA_LB_MAX_ROWS = 65536, /* queries x heads per sequence (mla_decode_lowbit_mq): a
+                              512-token prefill chunk at 128 heads */
   MLA_LB_NOALLOC_SCRATCH_BYTES = 64 << 20  /* per-GPU scratch of mla_decode_lowbit_noalloc */
 };
 
@@ -297,10 +298,15 @@ int mla_decode_lowbit_mq_workspace(int f, int32_t B, int32_t nq, int32_t H,
  * last block padded), the other counts on 16-row groups.
  *
  *   q_lat  [B][nq][H][512] bf16,  q_rope [B][nq][H][64] bf16
- *   nq >= 1 with nq*H <= MLA_LB_MAX_ROWS; H as in mla_decode_lowbit
+ *   nq >= 1 with nq*H <= MLA_LB_MAX_ROWS (65536 rows: a 512-token prefill
+ *          chunk at 128 heads, 4096 tokens at 16); H as in mla_decode_lowbit.
+ *          Each 128-row block reconstructs every page it reads, so a chunk of
+ *          C tokens at 128 heads costs C page reconstructions per page (vector
+ *          work of about a fifth of the block's matrix work)
  *   out    [B][nq][H][512] fp32,  lse [B][nq][H] fp32 (a query whose prefix
  *          is empty, L - nq + 1 + j <= 0, gets out 0 and lse -inf)
- *   workspace: at least mla_decode_lowbit_mq_workspace(...) bytes
+ *   workspace: at least mla_decode_lowbit_mq_workspace(...) bytes; a plan
+ *          whose workspace would pass 2^60 bytes is refused (MLA_LB_ESHAPE)
  *   other arguments and errors: as mla_decode_lowbit.
  */
 int mla_decode_lowbit_mq(int f, const uint16_t* q_lat, const uint16_t* q_rope,

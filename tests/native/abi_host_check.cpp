@@ -98,8 +98,10 @@ int main() {
   CHECK(mla_decode_lowbit_workspace(0, 65536, 16, 100, 0, &n) == MLA_LB_ESHAPE);
   CHECK(mla_decode_lowbit_workspace(0, 1, 20, 100, 0, &n) == MLA_LB_ESHAPE);
   CHECK(mla_decode_lowbit_workspace(0, 1, 16, 100, 0, nullptr) == MLA_LB_EINVAL);
-  CHECK(mla_decode_lowbit_mq_workspace(0, 2, 9, 128, 100, 0, &n) == MLA_LB_ESHAPE);
-  CHECK(mla_decode_lowbit_mq_workspace(0, 2, 8, 128, 100, 0, &n) == MLA_LB_OK);
+  CHECK(mla_decode_lowbit_mq_workspace(0, 2, 513, 128, 100, 0, &n) == MLA_LB_ESHAPE);
+  CHECK(mla_decode_lowbit_mq_workspace(0, 2, 512, 128, 100, 0, &n) == MLA_LB_OK);
+  CHECK(mla_decode_lowbit_mq_workspace(0, 65535, 512, 128, 2147483647, 2147483647, &n) ==
+        MLA_LB_ESHAPE);                                 // would pass 2^64 bytes
 
   // decode validation
   CHECK(mla_decode_lowbit(0, u16, u16, u8, 10, u16, 1, i32, i32, 1, i32, 65, 1, 16, 0.07f, 0,

@@ -135,9 +135,10 @@ def test_multi_query_validation(ops):
     assert call(f=3) == -3
     assert call(q_lat=None) == -1
     assert call(scale=0.0) == -1
-    for nq in (0, -1, 9):                  # 9 x 128 rows > MLA_LB_MAX_ROWS
+    for nq in (0, -1, 513):                # 513 x 128 rows > MLA_LB_MAX_ROWS (65536)
         assert call(nq=nq, H=128) == -2, nq
-    assert call(nq=65, H=16) == -2
+    assert call(nq=4097, H=16) == -2
+    assert ops.mla_decode_lowbit_mq_workspace("C4R4", 2, 512, 128, 200, 0) >= 0   # 65536 rows
     assert call(H=24) == -2
     need = ops.mla_decode_lowbit_mq_workspace("C4R4", 2, 4, 16, 200, 2)
     assert need == 2 * 2 * 64 * 516 * 4
@@ -167,11 +168,17 @@ def test_workspace_plan(ops):
         assert n % (B * H * 516 * 4) == 0
     with pytest.raises(ops.MlaLowbitError):
         ops.mla_decode_lowbit_workspace("C4R4", 1, 20, 100, 0)
-    # the largest plan the entry points accept (65535 sequences, 2^25 one-page
-    # splits, 1024 query rows) is sized exactly, below 2^63
+    # large plans are sized exactly up to 2^60 bytes and refused beyond (at
+    # 65535 sequences, 2^25 one-page splits and 65536 rows the product would
+    # pass 2^64)
     big = 2**31 - 1
-    n = ops.mla_decode_lowbit_mq_workspace("C4R4", 65535, 8, 128, big, big)
-    assert n == 65535 * 2**25 * 1024 * 516 * 4 and n < 2**63
+    n = ops.mla_decode_lowbit_mq_workspace("C4R4", 65535, 8, 128, big, 2**14)
+    assert n == 65535 * 2**14 * 1024 * 516 * 4 and n < 2**60
+    for nq, ns in ((8, big), (64, big), (512, big), (512, 2**17)):
+        with pytest.raises(ops.MlaLowbitError, match="ESHAPE"):
+            ops.mla_decode_lowbit_mq_workspace("C4R4", 65535, nq, 128, big, ns)
+    n = ops.mla_decode_lowbit_mq_workspace("C4R4", 4, 512, 128, 131072, 16)
+    assert n == 4 * 16 * 65536 * 516 * 4
     for call in (lambda: ops.mla_decode_lowbit_workspace("C4R4", 65536, 16, 1000, 0),
                  lambda: ops.mla_decode_lowbit_mq_workspace("C4R4", 65536, 2, 16, 1000, 0)):
         with pytest.raises(ops.MlaLowbitError):      # B beyond the grid limit

@@ -380,21 +380,23 @@ def test_multi_query_decode(fmt, nq, H):
             np.testing.assert_array_equal(lse[:, 0], l1)
 
 
-@pytest.mark.parametrize("nq,H", [(8, 128), (64, 16)])
-def test_multi_query_max_rows(nq, H):
-    """The largest call: nq * H = 1024 query rows per sequence (eight
-    128-row blocks), ragged lengths around the window edges, against the
-    oracle for every row, single-split and split."""
-    assert nq * H == 1024                          # MLA_LB_MAX_ROWS
-    lens = np.array([70, 133, 600])
-    d = synth.small(fmt="C4R4", batch=len(lens), heads=H, lens=lens, seed=82, queries=nq)
-    say("max rows", nq, H, lens.tolist())
+@pytest.mark.parametrize("nq,H", [(8, 128), (64, 16), (256, 16), (512, 128)])
+def test_multi_query_prefill_chunks(nq, H):
+    """Chunked prefill at real chunk sizes: nq new tokens per sequence, each
+    asking a query over its causal prefix, up to the largest call
+    (512 x 128 = 65536 query rows per sequence, MLA_LB_MAX_ROWS); lengths
+    shorter than the chunk (empty prefixes), around the window edge and
+    longer; every row against the oracle, single-split and split."""
+    lens = np.array([70, 133, 600]) if nq * H <= 1024 else np.array([300, nq + 133, 2000])
+    d = synth.small(fmt="C4R4", batch=len(lens), heads=H, lens=lens, seed=82 + nq, queries=nq)
+    say("prefill chunk", nq, H, lens.tolist())
     c = GpuCache(d)
     c.fill()
     for ns in (0, 1):
         out, lse = c.decode_mq(num_splits=ns)
         w = check_decode_mq(d, out, lse, lens)
         say("  num_splits", ns, "worst rel-L2", f"{w:.2e}")
+        del out, lse
 
 
 @pytest.mark.parametrize("H", [16, 128])
