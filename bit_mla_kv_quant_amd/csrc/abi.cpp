@@ -192,6 +192,9 @@ int decode_setup(int f, const uint16_t* q_lat, const uint16_t* q_rope, const uin
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.pps = plan.pps;
   a.nsplit = plan.nsplit;
+  // automatic plans of ragged batches of up to 64 sequences are dealt by
+  // length on the device (one wave reads every length)
+  a.balance = (num_splits == 0 && plan.nsplit > 1 && B <= 64) ? 1 : 0;
   a.out = out;
   a.lse = lse;
   a.new_c = new_c;

@@ -11,6 +11,7 @@
 #include "common.h"
 #include "dequant.h"
 #include "internal.h"
+#include "split_map.h"
 
 namespace mlb {
 
@@ -74,16 +75,16 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int hh = threadIdx.x >> 4, c = threadIdx.x & 15;
   const int h = blockIdx.y * 16 + hh;
   const int d0 = 64 * blockIdx.x + 4 * c;
-  const int ns = a.nsplit;
+  int first, ns;                                   // the sequence's workspace slots
+  split_range(a, b, threadIdx.x & 63, first, ns);
   float* o = a.out + ((int64_t)b * H + h) * DC + d0;
-  const int64_t base = (int64_t)b * ns * H + h;          // split jj at base + jj*H
+  const int64_t base = (int64_t)first * H + h;     // split jj at base + jj*H
   f32x4 accv = {0.f, 0.f, 0.f, 0.f};
   float ssum = 0.f, fsum = 0.f, M = -INFINITY;
-  if constexpr (NMAX > 0) {
-    combine_round<NMAX>(a, base, 0, ns, d0, M, accv, ssum, fsum);       // ns <= NMAX
-  } else {
-    for (int j0 = 0; j0 < ns; j0 += 16) combine_round<16>(a, base, j0, ns, d0, M, accv, ssum, fsum);
-  }
+  // rounds of NMAX (16 for NMAX = 0) partials in flight; one round when the
+  // sequence has at most NMAX splits (a balanced plan may give it more)
+  constexpr int R = NMAX > 0 ? NMAX : 16;
+  for (int j0 = 0; j0 < ns; j0 += R) combine_round<R>(a, base, j0, ns, d0, M, accv, ssum, fsum);
   if (M == -INFINITY) {                              // empty sequence
     *(f32x4*)o = f32x4{0.f, 0.f, 0.f, 0.f};
     if (blockIdx.x == 0 && c == 0) a.lse[(int64_t)b * H + h] = -INFINITY;

@@ -43,6 +43,7 @@
 #include "dequant.h"
 #include "internal.h"
 #include "quantize.h"
+#include "split_map.h"
 
 namespace mlb {
 
@@ -70,8 +71,12 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t ktile[2][PAGE * KT_PITCH];
   __shared__ int redo_flag;
 
-  const int j = blockIdx.x, b = blockIdx.y, hb = blockIdx.z;
+  const int hb = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the sequence and split of this workgroup's slot
+  const SplitSlot ss = split_slot(a, blockIdx.y * a.nsplit + blockIdx.x, lane);
+  if (ss.b < 0) return;                            // idle slot of a balanced plan
+  const int j = ss.j, b = ss.b;
   const int n16 = lane & 15, g = lane >> 4;        // reconstruction role
   const int tt = 16 * wave + n16;                  // this lane's token slot
   const int l32 = lane & 31, h = lane >> 5;        // attention role
@@ -82,13 +87,10 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
   const bool live = head < H;
   const int qrow = live ? head : 0;
 
-  const int L_in = a.seq_lens[b];
-  int L = L_in < 0 ? 0 : (L_in > a.max_seq_len ? a.max_seq_len : L_in);
-  const int sq = a.seq_slot[b];
-  if (sq < 0 || sq >= a.num_seq_slots) L = 0;
+  const int L = ss.L, sq = ss.sq;
   const int npages = (L + PAGE - 1) / PAGE;
-  const int p0 = j * a.pps;
-  const int p1 = min(p0 + a.pps, npages);
+  const int p0 = j * ss.pps;
+  const int p1 = min(p0 + ss.pps, npages);
   const bool single = a.nsplit == 1;
   const int rows_here = min(HB, H - HB * hb);      // rows past H are padding
   if (p0 >= p1) {
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
         *(f32x4*)(o + 4 * idx) = f32x4{0.f, 0.f, 0.f, 0.f};
       if (threadIdx.x < rows_here) a.lse[(int64_t)b * H + HB * hb + threadIdx.x] = -INFINITY;
     } else if (!single && threadIdx.x < rows_here) {   // no tokens: m = -inf for the merge
-      const int64_t base = ((int64_t)b * a.nsplit + j) * H + HB * hb + threadIdx.x;
+      const int64_t base = ((int64_t)ss.first + j) * H + HB * hb + threadIdx.x;
       *(f32x4*)(a.ws_ml + base * 4) = f32x4{-INFINITY, 0.f, 0.f, 0.f};
     }
     return;
@@ -110,13 +112,13 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
   // fused writer: token L-1 of a sequence whose length is within bounds (a
   // clamped length names a token the cache already holds: nothing is stored
   // or substituted, and the call decodes as mla_decode_lowbit)
-  const bool fused = a.new_c != nullptr && L_in <= a.max_seq_len;
+  const bool fused = a.new_c != nullptr && a.seq_lens[b] <= a.max_seq_len;
   // fused writer: the middle split of the sequence (first head block)
   // stores the newest token before its page loop.  No workgroup of this
   // launch reads those bytes; a middle split holds neither the sink tokens
   // nor the recent window, so it has time to spare; and this kernel has no
   // registers to spare for holding the row across the loop.
-  if (fused && j == (npages + a.pps - 1) / a.pps / 2 && hb == 0) {
+  if (fused && j == (npages + ss.pps - 1) / ss.pps / 2 && hb == 0) {
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     fused_store<F>(a, fused_load(a, b, wv, 4, lane), b, L, sq, wv, 4, lane);
   }
@@ -352,7 +354,7 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
       a.lse[(int64_t)b * H + head] =
           f_tot > 0.f ? (m_ref + __log2f(f_tot)) * 0.69314718055994531f : -INFINITY;
   } else {
-    const int64_t base = ((int64_t)b * a.nsplit + j) * H + head;
+    const int64_t base = ((int64_t)ss.first + j) * H + head;
     float* o = a.ws_o + base * DC + 4 * h;
 #pragma unroll
     for (int nt = 0; nt < 16; ++nt)

@@ -40,6 +40,7 @@
 #include "dequant.h"
 #include "internal.h"
 #include "quantize.h"
+#include "split_map.h"
 
 namespace mlb {
 
@@ -74,21 +75,22 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
   uint16_t* const qtile = lds + NW * QT * VT_PITCH;
 
-  const int j = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
+  const int hg = blockIdx.z;
   // wave index as a uniform value, so quarter indices and page ids stay in
-  // scalar registers (page ids then come from scalar loads)
+  // scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  // the sequence and split of this workgroup's slot
+  const SplitSlot ss = split_slot(a, blockIdx.y * a.nsplit + blockIdx.x, lane);
+  if (ss.b < 0) return;                            // idle slot of a balanced plan
+  const int j = ss.j, b = ss.b;
   const int n16 = lane & 15, g = lane >> 4;
   const int H = a.H;
 
-  const int L_in = a.seq_lens[b];
-  int L = L_in < 0 ? 0 : (L_in > a.max_seq_len ? a.max_seq_len : L_in);
-  const int sq = a.seq_slot[b];
-  if (sq < 0 || sq >= a.num_seq_slots) L = 0;
+  const int L = ss.L, sq = ss.sq;
   const int npages = (L + PAGE - 1) / PAGE;
-  const int p0 = j * a.pps;
-  const int p1 = min(p0 + a.pps, npages);
+  const int p0 = j * ss.pps;
+  const int p1 = min(p0 + ss.pps, npages);
   const bool single = a.nsplit == 1;
   if (p0 >= p1) {
     if (single && j == 0) {                        // empty sequence: out 0, lse -inf
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
         *(f32x4*)(o + 4 * idx) = f32x4{0.f, 0.f, 0.f, 0.f};
       if (threadIdx.x < 16) a.lse[(int64_t)b * H + 16 * hg + threadIdx.x] = -INFINITY;
     } else if (!single && threadIdx.x < 16) {      // no tokens: m = -inf for the merge
-      const int64_t base = ((int64_t)b * a.nsplit + j) * H + 16 * hg + threadIdx.x;
+      const int64_t base = ((int64_t)ss.first + j) * H + 16 * hg + threadIdx.x;
       *(f32x4*)(a.ws_ml + base * 4) = f32x4{-INFINITY, 0.f, 0.f, 0.f};
     }
     return;
@@ -109,12 +111,12 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
   // fused writer: token L-1 of a sequence whose length is within bounds (a
   // clamped length names a token the cache already holds: nothing is stored
   // or substituted, and the call decodes as mla_decode_lowbit)
-  const bool fused = a.new_c != nullptr && L_in <= a.max_seq_len;
+  const bool fused = a.new_c != nullptr && a.seq_lens[b] <= a.max_seq_len;
   // fused writer: the middle split of the sequence (first head block)
   // fetches the newest token now and stores it once its own work is done.
   // A middle split holds neither the sink tokens nor the recent window, so
   // it finishes ahead of the splits that do and the writer hides behind them.
-  const int nsplit_b = (npages + a.pps - 1) / a.pps;
+  const int nsplit_b = (npages + ss.pps - 1) / ss.pps;
   const bool writer = fused && j == nsplit_b / 2 && hg == 0;
   FusedRow fresh_row{};
   if (writer) fresh_row = fused_load(a, b, wave, NW, lane);
@@ -403,7 +405,7 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
     if ((threadIdx.x & 31) == 0)
       a.lse[(int64_t)b * H + head] = fs > 0.f ? (M + __log2f(fs)) * 0.69314718055994531f : -INFINITY;
   } else {
-    const int64_t base = ((int64_t)b * a.nsplit + j) * H + head;
+    const int64_t base = ((int64_t)ss.first + j) * H + head;
     dst = a.ws_o + base * DC;
     osc = 1.0f;
     if ((threadIdx.x & 31) == 0) *(f32x4*)(a.ws_ml + base * 4) = f32x4{M, fs, fs, 0.f};

@@ -39,6 +39,7 @@ struct DecodeArgs {
   float scale_log2;      // softmax_scale * log2(e)
   int32_t pps;           // pages per split
   int32_t nsplit;        // splits of a max_seq_len sequence (grid.x)
+  int32_t balance;       // deal the B * nsplit slots by sequence length (split_map.h)
   float* ws_o;           // [B][nsplit][H][512] unnormalised partial outputs
   float* ws_ml;          // [B][nsplit][H][4]   (max in log2 units, bf16-weight sum, fp32 sum, 0)
   float* out;            // [B][H][512]
