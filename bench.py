@@ -274,7 +274,7 @@ def main():
     ap.add_argument("--steps", type=int, default=3000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=4,
-                    help="synthetic workload id (0-6); default 4, the largest: 128K cache "
+                    help="synthetic workload id (0-7); default 4, the largest: 128K cache "
                          "pressure, B8 H128, append interleaved")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graphs")

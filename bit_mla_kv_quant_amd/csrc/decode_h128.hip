@@ -64,6 +64,17 @@ __device__ __forceinline__ float pair_max(float x) {
   return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
+// The lane's index, recomputed where it is needed: two instructions cost less
+// than holding lane-derived offsets across the page loop, where every
+// register is taken.  Values hoisted out of the loop spill, and each reload
+// waits on the vector memory counter, behind the packed-code loads in
+// flight.  The asm is volatile so that it is neither hoisted nor merged.
+__device__ __forceinline__ int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 }  // namespace
 
 template <int F>
@@ -79,6 +90,7 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
   const int j = ss.j, b = ss.b;
   const int n16 = lane & 15, g = lane >> 4;        // reconstruction role
   const int tt = 16 * wave + n16;                  // this lane's token slot
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int l32 = lane & 31, h = lane >> 5;        // attention role
   const int H = a.H;
   const int head = HB * hb + 32 * wave + l32;      // this lane's head
@@ -119,7 +131,6 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
   // nor the recent window, so it has time to spare; and this kernel has no
   // registers to spare for holding the row across the loop.
   if (fused && j == (npages + ss.pps - 1) / ss.pps / 2 && hb == 0) {
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
     fused_store<F>(a, fused_load(a, b, wv, 4, lane), b, L, sq, wv, 4, lane);
   }
 
@@ -146,6 +157,9 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
   // row tt, content dims 128g .. 128g+127 and RoPE dims 16g .. 16g+15.
   auto build = [&](auto ordinary_tag, const LaneSlot<F>& cur, const int k, const int phys) {
     constexpr bool ORDINARY = decltype(ordinary_tag)::value;
+    // the lane's slot and group pair, recomputed (see lane_here)
+    const int lid = lane_here();
+    const int tt = 16 * wv + (lid & 15), g = lid >> 4;
     uint16_t* row = ktile[k & 1] + tt * KT_PITCH;
     uint16_t* rc = row + 128 * g;
     uint16_t* rr = row + DC + 16 * g;
@@ -241,8 +255,9 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
       const uint16_t* ka = kb + (32 * c + l32) * KT_PITCH + 8 * h;
-      // K slices are read SPF slices ahead of their MFMA (LDS latency)
-      constexpr int SPF = 4;
+      // K slices are read SPF slices ahead of their MFMA (LDS latency; a
+      // fourth slice in flight costs the registers the C^T prefetch needs)
+      constexpr int SPF = 3;
       bf16x8 kn[SPF];
 #pragma unroll
       for (int s = 0; s < SPF; ++s) kn[s] = *(const bf16x8*)(ka + 16 * s);
@@ -285,15 +300,20 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
         }
         f_run += ft;
         const bf16x8 pa = bitcast<bf16x8>(phi), pl = bitcast<bf16x8>(plo);
-        // C^T operand: dim 32nt + l32, tokens 16q + 4h + 0..3 and 16q + 8 + 4h + 0..3
+        // C^T operand: dim 32nt + l32, tokens 16q + 4h + 0..3 and
+        // 16q + 8 + 4h + 0..3, read one dim tile ahead of its MFMAs
         const uint16_t* va = kb + (32 * c + 16 * q + 4 * h + (n16 >> 2)) * KT_PITCH +
                              16 * ((lane >> 4) & 1) + 4 * (n16 & 3);
         const uint16_t* vb = va + 8 * KT_PITCH;
+        bf16x4 cl = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)va);
+        bf16x4 ch = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vb);
 #pragma unroll
         for (int nt = 0; nt < 16; ++nt) {
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va + 32 * nt));
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + 32 * nt));
-          const bf16x8 ct = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 ct = __builtin_shufflevector(cl, ch, 0, 1, 2, 3, 4, 5, 6, 7);
+          if (nt + 1 < 16) {
+            cl = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va + 32 * (nt + 1)));
+            ch = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + 32 * (nt + 1)));
+          }
           acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ct, pa, acc[nt], 0, 0, 0);
           acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ct, pl, acc[nt], 0, 0, 0);
         }
