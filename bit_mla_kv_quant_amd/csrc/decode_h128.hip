@@ -333,9 +333,12 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
     if (threadIdx.x == 0) redo_flag = 0;
     pw.init(lane);
     int id_k = pw.id(0), id_k1 = pw.id(min(1, np - 1));
+    // pages 0 and 1 are requested together: page 1's codes must not wait
+    // for page 0's build
     LaneSlot<F> cur = load_lane_slot<F>(page_ptr(id_k), tt, g);
+    const LaneSlot<F> cur1 = load_lane_slot<F>(page_ptr(id_k1), tt, g);
     build_page(cur, 0, id_k);
-    cur = load_lane_slot<F>(page_ptr(id_k1), tt, g);
+    cur = cur1;
     __syncthreads();
     for (int k = 0; k < np; ++k) {
       pw.advance(min(k + 2, np - 1), lane);
