@@ -198,6 +198,26 @@ def test_split_invariance_and_determinism(fmt):
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4"])
+def test_split_invariance_128_rows(fmt):
+    """The 128-row kernel under several split plans, including one split of
+    141 pages (the block-table window refilled twice inside the page loop)
+    and a sequence shorter than the recent window."""
+    d = synth.small(fmt=fmt, batch=3, heads=128, lens=(9000, 3000, 130), seed=19)
+    say("split_invariance 128 rows", fmt)
+    c = GpuCache(d)
+    c.fill()
+    ref_out, ref_lse = c.decode(num_splits=1)
+    check_decode(d, c, ref_out, ref_lse, d.lens)
+    for ns in (3, 0, 70):
+        out, lse = c.decode(num_splits=ns)
+        w = check_decode(d, c, out, lse, d.lens)
+        worst = max(float(rel_l2_rows(out[b], ref_out[b]).max()) for b in range(d.B))
+        say("  num_splits", ns, "worst rel-L2 vs oracle", f"{w:.2e}", "vs one split", f"{worst:.2e}")
+        assert worst <= TOL_SPLIT, (ns, worst)
+        assert np.max(np.abs(lse - ref_lse)) <= TOL_SPLIT
+
+
 def test_sharp_attention():
     """Queries scaled x8: peaked softmax still within tolerance."""
     d = synth.small(fmt="C4R4", batch=2, heads=16, lens=(3000, 777), seed=12)
