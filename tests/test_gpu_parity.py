@@ -376,6 +376,39 @@ def check_decode_mq(d, out, lse, lens, which=None, fmt=None):
     return worst
 
 
+def test_randomized_sweep():
+    """Sixteen random calls from one fixed seed: format, heads (16-row and
+    128-row kernels), queries per sequence, ragged lengths from 0 to 6000
+    (sink, page and window edges among them), split count, shuffled sequence
+    slots, outlier strength and query scale.  Every row against the oracle."""
+    rng = np.random.default_rng(2027)
+    edge = [0, 1, 4, 5, 64, 132, 133, 197]
+    for case in range(16):
+        fmt = str(rng.choice(["C4R4", "C2R4", "C4R4F"]))
+        H = int(rng.choice([16, 32, 48, 64, 96, 128]))
+        nq = int(rng.choice([1, 1, 2, 3]))
+        B = int(rng.integers(1, 7))
+        lens = np.where(rng.random(B) < 0.3, rng.choice(edge, B), rng.integers(1, 6001, B))
+        ns = int(rng.choice([0, 0, 1, int(rng.integers(2, 10))]))
+        qscale = float(rng.choice([1.0, 3.0]))
+        # one spare page: a batch of empty sequences still has a page pool
+        d = synth.small(fmt=fmt, batch=B, heads=H, lens=lens, seed=3000 + case, queries=nq,
+                        outlier_factor=float(rng.choice([1.0, 8.0, 16.0])), spare_pages=1)
+        if qscale != 1.0:
+            d.q_lat = quant.f32_to_bf16(quant.bf16_to_f32(d.q_lat) * qscale)
+            d.q_rope = quant.f32_to_bf16(quant.bf16_to_f32(d.q_rope) * qscale)
+        say("sweep", case, fmt, "H", H, "nq", nq, "splits", ns, "q x", qscale, lens.tolist())
+        c = GpuCache(d, seq_slots=rng.permutation(B))
+        c.fill()
+        if nq == 1:
+            out, lse = c.decode(num_splits=ns)
+            w = check_decode(d, c, out, lse, lens)
+        else:
+            out, lse = c.decode_mq(num_splits=ns)
+            w = check_decode_mq(d, out, lse, lens)
+        say("  worst rel-L2", f"{w:.2e}")
+
+
 @pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "C4R4F"])
 @pytest.mark.parametrize("nq,H", [(1, 16), (2, 16), (3, 32), (4, 16), (2, 48), (3, 48), (8, 16), (2, 128)])
 def test_multi_query_decode(fmt, nq, H):
