@@ -99,32 +99,46 @@ __device__ __forceinline__ bf16x8 deq_int4x8_ubyte_ma(uint32_t w, float s, float
 
 // INT2 groups have four possible reconstructions; they are computed once per
 // group with the same arithmetic as above and kept as a byte-permute table:
-// bytes 0-3 = (x^(0), x^(1)) in `lo`, bytes 4-7 = (x^(2), x^(3)) in `hi`.
+// byte q of `lo` is the low byte of x^(q), byte q of `hi` its high byte.
 struct Lut2 {
-  uint32_t lo, hi;
+  uint32_t lo, hi;   // byte q: low / high byte of the bf16 value of code q
+  uint32_t sel_or;   // 0x04000400 in a vector register (see lut2_pair)
 };
 __device__ __forceinline__ Lut2 make_lut2(float s, float z) {
+  const uint32_t p01 = pack_bf16x2(__builtin_fmaf(0.0f, s, z), __builtin_fmaf(1.0f, s, z));
+  const uint32_t p23 = pack_bf16x2(__builtin_fmaf(2.0f, s, z), __builtin_fmaf(3.0f, s, z));
   Lut2 t;
-  t.lo = pack_bf16x2(__builtin_fmaf(0.0f, s, z), __builtin_fmaf(1.0f, s, z));
-  t.hi = pack_bf16x2(__builtin_fmaf(2.0f, s, z), __builtin_fmaf(3.0f, s, z));
+  t.lo = __builtin_amdgcn_perm(p23, p01, 0x06040200u);   // bytes 0, 2, 4, 6 of {p23, p01}
+  t.hi = __builtin_amdgcn_perm(p23, p01, 0x07050301u);   // bytes 1, 3, 5, 7
+  asm volatile("v_mov_b32 %0, 0x4000400" : "=v"(t.sel_or));
   return t;
 }
 
-// Two INT2 codes a (bits 0-1) and b (bits 16-17) of `t` -> bf16 pair
-// (x^(a), x^(b)).  Selector bytes (2a, 2a+1, 2b, 2b+1) pick the table entries.
-__device__ __forceinline__ uint32_t lut2_pair(uint32_t t, const Lut2& lut) {
-  const uint32_t sel = t * 0x202u + 0x01000100u;
+// Two INT2 codes a (bits 0-1 of bytes 0 and 1 of `d`) and b (same bits of
+// bytes 2 and 3) -> bf16 pair (x^(a), x^(b)).  One AND-OR turns d into the
+// selector bytes (a, a + 4, b, b + 4): low byte from lut.lo, high byte from
+// lut.hi.
+// The AND-OR is one v_and_or_b32; its two constants cannot both be literals
+// or scalar registers, so the OR constant comes in a vector register.
+__device__ __forceinline__ uint32_t lut2_pair(uint32_t d, const Lut2& lut) {
+  uint32_t sel;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(sel) : "v"(d), "s"(0x03030303u), "v"(lut.sel_or));
   return __builtin_amdgcn_perm(lut.hi, lut.lo, sel);
 }
 
 // 16 INT2 codes of one 32-bit word (dim 2m in bits 2m, dim 2m+1 in bits
-// 16+2m) -> dims 0..7 in `a`, dims 8..15 in `b`.
+// 16+2m) -> dims 0..7 in `a`, dims 8..15 in `b`.  The bytes holding the codes
+// are first doubled (byte 0 into bytes 0 and 1, byte 2 into bytes 2 and 3;
+// likewise bytes 1 and 3), so one shift brings a code pair into selector
+// position.
 __device__ __forceinline__ void deq_int2x16(uint32_t w, const Lut2& lut, bf16x8& a, bf16x8& b) {
+  const uint32_t dl = __builtin_amdgcn_perm(w, w, 0x02020000u);
+  const uint32_t dh = __builtin_amdgcn_perm(w, w, 0x03030101u);
   u32x4 r, t;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) r[m] = lut2_pair((w >> (2 * m)) & 0x00030003u, lut);
+  for (int m = 0; m < 4; ++m) r[m] = lut2_pair(dl >> (2 * m), lut);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) t[m] = lut2_pair((w >> (2 * m + 8)) & 0x00030003u, lut);
+  for (int m = 0; m < 4; ++m) t[m] = lut2_pair(dh >> (2 * m), lut);
   a = bitcast<bf16x8>(r);
   b = bitcast<bf16x8>(t);
 }
@@ -212,29 +226,6 @@ __device__ __forceinline__ LaneSlot<F> load_lane_slot(const uint8_t* pg, int tt,
   if constexpr (FM::F32R) p.mr = *(const u32x2*)(pg + FM::OFF_MR + tt * 8);
   else p.mr = *(const uint32_t*)(pg + FM::OFF_MR + tt * 4);
   return p;
-}
-
-// One half of load_lane_slot: PART 0 loads content group 2g (the first 64
-// of the lane's 128 content dims), both content groups' metadata and the
-// RoPE codes and metadata; PART 1 loads content group 2g+1.  Other fields of
-// p are left as they are.
-template <int F, int PART>
-__device__ __forceinline__ void load_lane_slot_half(LaneSlot<F>& p, const uint8_t* pg, int tt,
-                                                    int g) {
-  using FM = Fmt<F>;
-  if constexpr (FM::CBITS == 4) {
-    const uint8_t* row = pg + (g * PAGE + tt) * 64 + 32 * PART;
-    p.c[2 * PART] = *(const u32x4*)row;
-    p.c[2 * PART + 1] = *(const u32x4*)(row + 16);
-  } else {
-    p.c[PART] = *(const u32x4*)(pg + ((g >> 1) * PAGE + tt) * 64 + 32 * (g & 1) + 16 * PART);
-  }
-  if constexpr (PART == 0) {
-    p.r = *(const u32x2*)(pg + FM::OFF_R + tt * 32 + 8 * g);
-    p.mc = *(const u32x2*)(pg + FM::OFF_MC + tt * 32 + 8 * g);
-    if constexpr (FM::F32R) p.mr = *(const u32x2*)(pg + FM::OFF_MR + tt * 8);
-    else p.mr = *(const uint32_t*)(pg + FM::OFF_MR + tt * 4);
-  }
 }
 
 // (scale, zero) of a group: a bf16 pair in one word, or fp32 bit patterns
