@@ -267,12 +267,14 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
         if (s + SPF < 36) kn[s % SPF] = *(const bf16x8*)(ka + 16 * (s + SPF));
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qv[s], sacc, 0, 0, 0);
       }
-      const int i_base = (p0 + k) * PAGE + 32 * c + 4 * h;
+      // scores in log2 units; tokens past the row's prefix (or on an
+      // unusable page) are -inf.  Register r holds token offset
+      // 8(r/4) + r%4 past lim's origin, a constant, so each score costs one
+      // compare against the chunk's limit.
+      const int lim = phys >= 0 ? L_row - ((p0 + k) * PAGE + 32 * c + 4 * h) : 0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = i_base + 8 * (r >> 2) + (r & 3);
-        sacc[r] = (phys >= 0 && i < L_row) ? sacc[r] * a.scale_log2 : -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        sacc[r] = 8 * (r >> 2) + (r & 3) < lim ? sacc[r] * a.scale_log2 : -INFINITY;
       float tm = sacc[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) tm = fmaxf(tm, sacc[r]);

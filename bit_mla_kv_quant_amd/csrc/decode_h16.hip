@@ -281,11 +281,16 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
   // i0 + 4g + v, head n16) and the content rows in the wave's tile
   auto aggregate = [&](const int q, const int phys, const f32x4 sc) {
     const int i0 = (p0 + (q >> 2)) * PAGE + QT * (q & 3);
+    // scores in log2 units; tokens past the row's prefix (or an unusable
+    // page) then become -inf -- a branch taken only at a prefix's end
     float x[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int i = i0 + 4 * g + v;
-      x[v] = (phys >= 0 && i < L_row) ? sc[v] * a.scale_log2 : -INFINITY;
+    for (int v = 0; v < 4; ++v) x[v] = sc[v] * a.scale_log2;
+    if (phys < 0 || !__all(i0 + QT <= L_row)) {
+      const int lim = phys >= 0 ? L_row - i0 - 4 * g : 0;        // live offsets < lim
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (v >= lim) x[v] = -INFINITY;
     }
     const float tm = head_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
     // first live quarter of the head sets its reference (all earlier weights
