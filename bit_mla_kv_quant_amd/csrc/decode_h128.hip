@@ -233,8 +233,39 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
              meta_scale(cur.mc[1]) * 512.0f <= FP8_PATH_MAX_SCALE9;
     return !__any(!fits);
   };
+  // Are all of this wave's slots of page k protected (recent-window or sink
+  // rows, the fused writer's token among them)?
+  auto all_protected = [&](const int k, const int phys) -> bool {
+    const int i = (p0 + k) * PAGE + 16 * wv + (lane_here() & 15);
+    return __all(phys >= 0 && i < L && is_protected(i, L));
+  };
+  // such a page has nothing to reconstruct: its BF16 rows are copied with
+  // the loads in three batches of six slices (one memory latency per batch,
+  // not one per slice)
+  auto copy_protected = [&](const int k) {
+    const int lid = lane_here();
+    const int tt = 16 * wv + (lid & 15), g = lid >> 4;
+    const int i = (p0 + k) * PAGE + tt;
+    uint16_t* row = ktile[k & 1] + tt * KT_PITCH;
+    const bool fresh = fused && i == L - 1;
+    const uint16_t* prow = prot_seq + (int64_t)prot_row(i) * DROW;
+    const uint16_t* pc = (fresh ? a.new_c + (int64_t)b * DC : prow) + 128 * g;
+    const uint16_t* pr = (fresh ? a.new_r + (int64_t)b * DR : prow + DC) + 16 * g;
+#pragma unroll
+    for (int t0 = 0; t0 < 18; t0 += 6) {
+      bf16x8 v[6];
+#pragma unroll
+      for (int t = 0; t < 6; ++t)
+        v[t] = *(const bf16x8*)(t0 + t < 16 ? pc + 8 * (t0 + t) : pr + 8 * (t0 + t - 16));
+#pragma unroll
+      for (int t = 0; t < 6; ++t)
+        *(bf16x8*)(t0 + t < 16 ? row + 128 * g + 8 * (t0 + t) : row + DC + 16 * g + 8 * (t0 + t - 16)) = v[t];
+      __builtin_amdgcn_sched_barrier(0);   // the next batch's loads stay below
+    }
+  };
   auto build_page = [&](const LaneSlot<F>& cur, const int k, const int phys) {
     if (ordinary(cur, k, phys)) build(std::true_type{}, cur, k, phys);
+    else if (all_protected(k, phys)) copy_protected(k);
     else build(std::false_type{}, cur, k, phys);
   };
 
