@@ -223,10 +223,14 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
       *(bf16x8*)(rr + 8) = fix(deq_int4x8(cur.r[1], cur.mr), DC + 16 * g + 8);
     }
   };
-  // Is page k ordinary for this wave (decided from its packed metadata)?
+  // Is page k ordinary for this wave: are its 16 slots all packed tokens
+  // (none a sink, none in the recent window, all within the length) whose
+  // scales suit the fp8 path?  Decided per wave, so on the page holding the
+  // sinks or the window's start only the waves with such slots leave the
+  // fast path.
   auto ordinary = [&](const LaneSlot<F>& cur, const int k, const int phys) -> bool {
-    const int p = p0 + k;
-    if (phys < 0 || p * PAGE < NSINK || (p + 1) * PAGE > L - NRECENT) return false;
+    const int i0 = (p0 + k) * PAGE + 16 * wv;
+    if (phys < 0 || i0 < NSINK || i0 + 16 > L - NRECENT) return false;
     bool fits = meta_scale(cur.mr) * 512.0f <= FP8_PATH_MAX_SCALE9;
     if constexpr (Fmt<F>::CBITS == 4)
       fits = fits && meta_scale(cur.mc[0]) * 512.0f <= FP8_PATH_MAX_SCALE9 &&
