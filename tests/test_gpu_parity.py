@@ -257,13 +257,15 @@ def test_score_jumps(H):
 
 
 @pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "C4R4F"])
-def test_token_aging(fmt):
+@pytest.mark.parametrize("H", [16, 128])
+def test_token_aging(fmt, H):
     """Append one token per step from L=1 to 300 and decode each step: a
     token's packed bytes never change after insertion, tokens leaving the
-    recent window switch to their packed copy, and every step matches."""
+    recent window switch to their packed copy (the protection buffer's ring
+    wraps past 132 rows), and every step matches, on both kernels."""
     steps = 300
-    d = synth.small(fmt=fmt, batch=1, heads=16, lens=(0,), seed=21, extra_tokens=steps)
-    say("token_aging", fmt)
+    d = synth.small(fmt=fmt, batch=1, heads=H, lens=(0,), seed=21, extra_tokens=steps)
+    say("token_aging", fmt, H)
     c = GpuCache(d)
     prev = None
     for L in range(1, steps + 1):
