@@ -14,7 +14,8 @@
 //      (n16, g) owns slot 16w + n16 and, in it, content groups 2g and 2g+1
 //      (dims 128g .. 128g+127) and RoPE dims 16g .. 16g+15, from packed codes
 //      loaded one step earlier.  Protected tokens take their BF16 row
-//      instead, unusable slots zeros.
+//      instead (a wave whose 16 slots are all protected only copies rows),
+//      unusable slots zeros.
 //   attend page k -- wave w owns heads 32w .. 32w+31 of the block, with
 //      v_mfma_f32_32x32x16_bf16.  Scores are formed transposed,
 //      S^T[tokens][heads] = K . Q^T (K slices read from the tile, the query
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(256, 1) void decode128_kernel(DecodeArgs a) {
       for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
       const uint16_t* ka = kb + (32 * c + l32) * KT_PITCH + 8 * h;
       // K slices are read SPF slices ahead of their MFMA (LDS latency; a
-      // fourth slice in flight costs the registers the C^T prefetch needs)
+      // fourth slice in flight measured no faster)
       constexpr int SPF = 3;
       bf16x8 kn[SPF];
 #pragma unroll
