@@ -353,15 +353,15 @@ __global__ __launch_bounds__(512, 1) void decode16w_kernel(DecodeArgs a) {
     if (wave < nquart) {
       LaneSlot<F> cur = load_quarter(wave);
       for (int q = wave; q < nquart; q += NW) {
-        // the two waves of a SIMD take turns at the higher issue priority, so
-        // neither finishes its quarters far ahead of the other
-        if (((q >> 3) ^ (wave >> 2)) & 1) __builtin_amdgcn_s_setprio(1);
-        else __builtin_amdgcn_s_setprio(0);
+        // a wave reconstructing and scoring issues ahead of the other wave on
+        // its SIMD; a wave aggregating fills the issue slots that leaves
+        __builtin_amdgcn_s_setprio(1);
         const int phys = pw.id(q >> 2);
         pw.advance((q + NW < nquart ? q + NW : q) >> 2, lane);
         const f32x4 sc = ordinary(q, phys, cur) ? quarter(std::true_type{}, q, phys, cur)
                                                 : quarter(std::false_type{}, q, phys, cur);
         cur = load_quarter(q + NW < nquart ? q + NW : q);
+        __builtin_amdgcn_s_setprio(0);
         aggregate(q, phys, sc);
       }
     }
