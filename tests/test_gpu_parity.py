@@ -414,14 +414,16 @@ def test_randomized_sweep(seed):
 
 
 @pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "C4R4F"])
-@pytest.mark.parametrize("nq,H", [(1, 16), (2, 16), (3, 32), (4, 16), (2, 48), (3, 48), (8, 16), (2, 128)])
+@pytest.mark.parametrize("nq,H", [(1, 16), (2, 16), (3, 32), (4, 16), (2, 48), (3, 48), (8, 16), (2, 128),
+                                  (11, 16), (5, 48)])
 def test_multi_query_decode(fmt, nq, H):
     """nq queries per sequence, each over its causal prefix, against the
     oracle; lengths below nq (empty prefixes), at sink / page / window edges
     and over several splits.  Up to 80 rows and 144 rows take the 16-row
     kernel; 96 and 128 rows take the 128-row one, 2 x 48 = 96 rows padded to
-    128 with a query boundary inside the block; nq = 1 must equal
-    mla_decode_lowbit."""
+    128 with a query boundary inside the block; 176 and 240 rows take two
+    128-row blocks with the second padded, and at 5 x 48 the third query's
+    heads straddle the two blocks; nq = 1 must equal mla_decode_lowbit."""
     lens = np.array([1, 3, 8, 9, 64, 65, 133, 140, 300, 1000])
     d = synth.small(fmt=fmt, batch=len(lens), heads=H, lens=lens, seed=51 + nq, queries=nq)
     say("multi_query", fmt, nq, H, lens.tolist())
