@@ -156,8 +156,12 @@ EDGE_LENS = (0, 1, 3, 4, 5, 63, 64, 65, 127, 128, 129, 131, 132, 133, 200, 1000)
 
 
 @pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "C4R4F"])
-@pytest.mark.parametrize("H", [16, 32, 64, 96, 128])
+@pytest.mark.parametrize("H", [16, 32, 64, 80, 96, 112, 128])
 def test_decode_edge_lengths(fmt, H):
+    """Every edge length (empty, sinks only, page and recent-window
+    boundaries) at head counts routed to the 16-row kernel (16-80) and to the
+    128-row kernel (96, 112 padded to a 128-row block; 128), over 1, 3 and
+    the automatic number of splits."""
     d = synth.small(fmt=fmt, batch=len(EDGE_LENS), heads=H, lens=EDGE_LENS, seed=H)
     say("decode_edge", fmt, H)
     c = GpuCache(d, seq_slots=np.random.default_rng(H).permutation(d.B))
